@@ -1,0 +1,320 @@
+"""Pins of the CPU oracle against what the Mixtral of Experts pages and plain
+mathematics fix, written so that tests can run them against the oracle as
+built and against deliberately broken copies of it.
+
+Each check raises AssertionError on a mismatch.  None of them re-types the
+oracle's code: the comparisons are against library routines (numpy, scipy,
+torch CPU in float64), brute force over every expert, closed forms, and
+invariants of a per-token function.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+import oracle
+from sparse_mixture_experts_select_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+# ---------------------------------------------------------------- fixtures
+
+
+def random_case(T, d, f, E, seed, dtype="f32", scale_router=1.0):
+    """Random float32 (or bf16-bit) layer inputs drawn with numpy."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((d, E)) * scale_router / math.sqrt(d)).astype(np.float32)
+    w1 = (rng.standard_normal((E, d, f)) / math.sqrt(d)).astype(np.float32)
+    w3 = (rng.standard_normal((E, d, f)) / math.sqrt(d)).astype(np.float32)
+    w2 = (rng.standard_normal((E, f, d)) / math.sqrt(f)).astype(np.float32)
+    case = {"x": x, "w_router": wr, "w1": w1, "w3": w3, "w2": w2}
+    if dtype == "bf16":
+        case = {kk: inputs.host_array(torch.from_numpy(v).to(torch.bfloat16)) for kk, v in case.items()}
+    return case
+
+
+def f64(a):
+    """Exact float64 view of an oracle input (float32 or bf16 bits)."""
+    if a.dtype == np.uint16:
+        return inputs.bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+# ------------------------------------------------- independent references
+
+
+def dense_expert_outputs(x, w1, w3, w2):
+    """Every token through every expert, with numpy matmuls and scipy's
+    logistic function: y[e] = (z * expit(z)) * (x @ w3[e]) @ w2[e], z = x @ w1[e]."""
+    E = w1.shape[0]
+    ys = []
+    for e in range(E):
+        z = x @ w1[e]
+        ys.append(((z * scipy.special.expit(z)) * (x @ w3[e])) @ w2[e])
+    return np.stack(ys, 0)  # [E,T,d]
+
+
+def brute_force_layer(case, k, bias=None):
+    """Masked top-k mixture: all E experts evaluated densely, logits outside
+    the k largest set to -inf, softmax over all E, weighted sum over all E."""
+    x, wr = f64(case["x"]), f64(case["w_router"])
+    w1, w3, w2 = f64(case["w1"]), f64(case["w3"]), f64(case["w2"])
+    logits = x @ wr
+    if bias is not None:
+        logits = logits + np.asarray(bias, np.float64)[None, :]
+    T, E = logits.shape
+    order = np.argsort(-logits.astype(np.float32), axis=1, kind="stable")[:, :k]
+    masked = np.full_like(logits, -np.inf)
+    rows = np.arange(T)[:, None]
+    masked[rows, order] = logits[rows, order]
+    weights = scipy.special.softmax(masked, axis=1)
+    ys = dense_expert_outputs(x, w1, w3, w2)
+    out = np.einsum("te,etd->td", weights, ys)
+    return out, order, weights, logits
+
+
+def torch_dense_swiglu(x, w1, w3, w2):
+    """(silu(x @ w1) * (x @ w3)) @ w2 with torch CPU float64."""
+    X = torch.from_numpy(f64(x))
+    A = torch.from_numpy(f64(w1))
+    B = torch.from_numpy(f64(w3))
+    C = torch.from_numpy(f64(w2))
+    return ((torch.nn.functional.silu(X @ A) * (X @ B)) @ C).numpy()
+
+
+# ------------------------------------------------------------------- pins
+
+
+def check_gate_invariants(seed=1):
+    """Gates are non-negative, sum to 1, come in descending order, and for
+    k=2 equal the logistic function of the logit gap (softmax over the two
+    kept logits, section 2.1 display 2)."""
+    c = random_case(200, 32, 16, 8, seed, scale_router=3.0)
+    logits, ids, gates = oracle.route(c["x"], c["w_router"], 2)
+    assert np.all(gates >= 0)
+    assert np.allclose(gates.sum(1), 1.0, atol=1e-12, rtol=0)
+    assert np.all(gates[:, 0] >= gates[:, 1])
+    l1 = logits[np.arange(200), ids[:, 0]]
+    l2 = logits[np.arange(200), ids[:, 1]]
+    assert np.all(l1 >= l2)
+    assert np.allclose(gates[:, 0], scipy.special.expit(l1 - l2), atol=1e-14, rtol=0)
+    # the kept pair is the largest pair: no other logit exceeds the second
+    for t in range(200):
+        others = np.delete(logits[t], ids[t])
+        assert np.all(others.astype(np.float32) <= np.float32(l2[t]))
+
+
+def check_k_distinct(seed=2):
+    """Exactly k distinct experts per token; counts sum to T*k."""
+    for k in (1, 2, 3, 8):
+        c = random_case(150, 16, 8, 8, seed + k)
+        _, ids, _ = oracle.route(c["x"], c["w_router"], k)
+        assert ids.shape == (150, k)
+        for t in range(150):
+            assert len(set(ids[t].tolist())) == k
+            assert ids[t].min() >= 0 and ids[t].max() < 8
+        counts = np.bincount(ids.ravel(), minlength=8)
+        assert counts.sum() == 150 * k
+
+
+def check_brute_force(seed=3, dtype="f32"):
+    """Oracle = brute force over every expert with masked top-k (tiny sizes)."""
+    for (T, d, f, E, k) in [(33, 24, 40, 8, 2), (17, 16, 24, 6, 3), (9, 8, 8, 4, 1)]:
+        c = random_case(T, d, f, E, seed + E, dtype)
+        ref, order, weights, _ = brute_force_layer(c, k)
+        r = oracle.moe_tokens(c["x"], c["w_router"], c["w1"], c["w3"], c["w2"], k)
+        np.testing.assert_array_equal(r["ids"], order)
+        assert np.allclose(r["gates"], weights[np.arange(T)[:, None], order], atol=1e-13, rtol=0)
+        scale = np.abs(ref).max()
+        assert np.abs(r["out"] - ref).max() <= 1e-11 * scale
+
+
+def check_identical_experts(seed=4):
+    """All experts equal => the layer is one dense SwiGLU FFN (gates sum to 1)."""
+    c = random_case(40, 32, 48, 8, seed)
+    for name in ("w1", "w3", "w2"):
+        c[name] = np.repeat(c[name][:1], 8, axis=0).copy()
+    r = oracle.moe_tokens(c["x"], c["w_router"], c["w1"], c["w3"], c["w2"], 2)
+    ref = torch_dense_swiglu(c["x"], c["w1"][0], c["w3"][0], c["w2"][0])
+    assert np.abs(r["out"] - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def check_special_k(seed=5):
+    """k=1: gate 1 and the argmax expert alone.  k=E: dense softmax mixture.
+    E=1: plain SwiGLU."""
+    c = random_case(30, 16, 32, 5, seed)
+    x, wr = f64(c["x"]), f64(c["w_router"])
+    ys = dense_expert_outputs(x, f64(c["w1"]), f64(c["w3"]), f64(c["w2"]))
+    logits = x @ wr
+    r1 = oracle.moe_tokens(c["x"], c["w_router"], c["w1"], c["w3"], c["w2"], 1)
+    assert np.all(r1["gates"] == 1.0)
+    am = np.argmax(logits.astype(np.float32), axis=1)
+    np.testing.assert_array_equal(r1["ids"][:, 0], am)
+    ref1 = ys[am, np.arange(30)]
+    assert np.abs(r1["out"] - ref1).max() <= 1e-12 * np.abs(ref1).max()
+    rE = oracle.moe_tokens(c["x"], c["w_router"], c["w1"], c["w3"], c["w2"], 5)
+    w = scipy.special.softmax(logits, axis=1)
+    refE = np.einsum("te,etd->td", w, ys)
+    assert np.abs(rE["out"] - refE).max() <= 1e-12 * np.abs(refE).max()
+    c1 = random_case(12, 16, 24, 1, seed + 1)
+    r = oracle.moe_tokens(c1["x"], c1["w_router"], c1["w1"], c1["w3"], c1["w2"], 1)
+    ref = torch_dense_swiglu(c1["x"], c1["w1"][0], c1["w3"][0], c1["w2"][0])
+    assert np.abs(r["out"] - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def check_all_ties(seed=6):
+    """w_router = 0: every logit ties, the lowest indices win, gates are 1/2."""
+    c = random_case(25, 16, 8, 8, seed)
+    c["w_router"] = np.zeros_like(c["w_router"])
+    _, ids, gates = oracle.route(c["x"], c["w_router"], 2)
+    assert np.all(ids[:, 0] == 0) and np.all(ids[:, 1] == 1)
+    assert np.all(gates == 0.5)
+    counts = np.bincount(ids.ravel(), minlength=8)
+    np.testing.assert_array_equal(counts, [25, 25, 0, 0, 0, 0, 0, 0])
+
+
+def check_bias(seed=7):
+    """A large additive bias on one expert makes it every token's first pick."""
+    c = random_case(60, 16, 8, 8, seed)
+    bias = np.zeros(8, np.float32)
+    bias[5] = 50.0
+    logits, ids, gates = oracle.route(c["x"], c["w_router"], 2, bias=bias)
+    assert np.all(ids[:, 0] == 5)
+    ref_l = f64(c["x"]) @ f64(c["w_router"])
+    assert np.allclose(logits - ref_l, bias[None, :].astype(np.float64), atol=1e-12)
+    second = np.argsort(-np.delete(ref_l, 5, axis=1).astype(np.float32), axis=1, kind="stable")[:, 0]
+    second = np.where(second >= 5, second + 1, second)
+    np.testing.assert_array_equal(ids[:, 1], second)
+    assert np.all(gates[:, 0] > 0.999)
+
+
+def check_invariances(seed=8):
+    """Token permutation permutes outputs; relabelling experts together with
+    the router columns leaves outputs unchanged; scaling w2 by 2 doubles them."""
+    c = random_case(40, 24, 32, 8, seed)
+    base = oracle.moe_tokens(c["x"], c["w_router"], c["w1"], c["w3"], c["w2"], 2)
+    perm = np.random.default_rng(seed).permutation(40)
+    rp = oracle.moe_tokens(c["x"][perm], c["w_router"], c["w1"], c["w3"], c["w2"], 2)
+    np.testing.assert_array_equal(rp["out"], base["out"][perm])
+    ep = np.random.default_rng(seed + 1).permutation(8)
+    re = oracle.moe_tokens(c["x"], c["w_router"][:, ep], c["w1"][ep], c["w3"][ep], c["w2"][ep], 2)
+    np.testing.assert_array_equal(ep[re["ids"]], base["ids"])
+    np.testing.assert_array_equal(re["out"], base["out"])
+    r2 = oracle.moe_tokens(c["x"], c["w_router"], c["w1"], c["w3"], c["w2"] * 2, 2)
+    np.testing.assert_array_equal(r2["out"], 2 * base["out"])
+
+
+def check_silu():
+    """SiLU through a 1x1 layer (d=f=E=k=1, unit weights): out = SiLU(z).
+    SiLU(0) = 0, SiLU(z) -> z for large z, -> 0 for very negative z, and
+    z * logistic(z) in between (SwiGLU pseudocode: SiLU on the w1 branch)."""
+    one = np.ones((1, 1, 1), np.float32)
+    for z in (0.0, -30.0, 30.0, 1.5, -2.25, 0.375):
+        x = np.array([[1.0]], np.float32)
+        w1 = np.array([[[z]]], np.float32)
+        r = oracle.moe_tokens(x, np.ones((1, 1), np.float32), w1, one, one, 1)
+        got = r["out"][0, 0]
+        want = z * scipy.special.expit(z)
+        assert abs(got - want) <= 1e-15 * max(1.0, abs(want)), (z, got, want)
+    # the w3 branch is linear: scaling it scales the output
+    x = np.array([[1.0]], np.float32)
+    w1 = np.array([[[1.5]]], np.float32)
+    r = oracle.moe_tokens(x, np.ones((1, 1), np.float32), w1, 3 * one, one, 1)
+    assert abs(r["out"][0, 0] - 3 * 1.5 * scipy.special.expit(1.5)) < 1e-14
+
+
+def check_forced(seed=9):
+    """Forcing the oracle's own selection reproduces the routed result, and
+    per-slot expert outputs recombine to the output."""
+    c = random_case(20, 16, 24, 8, seed)
+    r = oracle.moe_tokens(c["x"], c["w_router"], c["w1"], c["w3"], c["w2"], 2, want_y=True, want_h=True)
+    tok = np.array([3, 0, 19, 7], np.int64)
+    rf = oracle.moe_tokens(c["x"], None, c["w1"], c["w3"], c["w2"], 2, tokens=tok,
+                           forced_ids=r["ids"][tok], forced_gates=r["gates"][tok], want_y=True)
+    np.testing.assert_array_equal(rf["out"], r["out"][tok])
+    np.testing.assert_array_equal(rf["y"], r["y"][tok])
+    ys = dense_expert_outputs(f64(c["x"]), f64(c["w1"]), f64(c["w3"]), f64(c["w2"]))
+    for s in range(20):
+        for j in range(2):
+            e = r["ids"][s, j]
+            assert np.abs(r["y"][s, j] - ys[e, s]).max() <= 1e-12 * np.abs(ys[e, s]).max()
+
+
+def check_rmsnorm(seed=10):
+    """Unit-gain RMSNorm against torch's rms_norm and a constant-row closed form."""
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((17, 64)).astype(np.float32) * 3
+    got = oracle.rmsnorm(h, 1e-5)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(h.astype(np.float64)), (64,), eps=1e-5).numpy()
+    assert np.abs(got - want).max() <= 1e-13
+    const = np.full((2, 32), 0.5, np.float32)
+    got = oracle.rmsnorm(const, 1e-5)
+    assert np.allclose(got, 0.5 / math.sqrt(0.25 + 1e-5), atol=1e-15, rtol=0)
+
+
+def uniform_routing_stats(T=16384, seed=0):
+    """Routing of unit-RMS synthetic tokens with an unbiased router at the
+    pages' width d=4096, E=8, k=2."""
+    x = inputs.make_x(T, 4096, torch.float32, "cpu", "rms", seed, "routing_stats")
+    wr = inputs.make_router(4096, 8, torch.float32, "cpu", seed, "routing_stats")
+    _, ids, _ = oracle.route(inputs.host_array(x), inputs.host_array(wr), 2)
+    first_repeat = float(np.mean(ids[1:, 0] == ids[:-1, 0]))
+    either = [len(set(ids[t]) & set(ids[t + 1])) > 0 for t in range(T - 1)]
+    shares = np.bincount(ids.ravel(), minlength=8) / (2.0 * T)
+    return first_repeat, float(np.mean(either)), shares
+
+
+def check_uniform_routing():
+    """Against the pages' uniform-routing references (first choice repeats
+    about 12.5%, first-or-second about 46%) and the closed forms 1/8 and
+    1 - C(6,2)/C(8,2) = 13/28 for independent tokens."""
+    g = golden("pages_facts.json")["uniform_routing"]
+    first, either, shares = uniform_routing_stats()
+    n = 16383
+    sig1 = math.sqrt(0.125 * 0.875 / n)
+    p2 = 1 - math.comb(6, 2) / math.comb(8, 2)
+    sig2 = math.sqrt(p2 * (1 - p2) / n)
+    assert abs(first - g["first_choice_repeat"]) < 4 * sig1, first
+    assert abs(p2 - g["first_or_second_repeat_about"]) < 0.005
+    assert abs(either - p2) < 4 * sig2, either
+    assert np.all(np.abs(shares - 0.125) < 0.02), shares
+
+
+def check_parameter_counts():
+    """The hyperparameter table's shapes give the pages' ~47B total and ~13B
+    active parameters (experts, grouped-query attention, router, norms,
+    input and output embeddings), and the bf16 workloads use those shapes."""
+    hp = golden("pages_facts.json")["hyperparameters"]
+    pc = golden("pages_facts.json")["parameter_counts"]
+    d, f, E, k = hp["dim"], hp["hidden_dim"], hp["n_experts"], hp["top_k"]
+    L, V = hp["n_layers"], hp["vocab_size"]
+    hd, nh, nkv = hp["head_dim"], hp["n_heads"], hp["n_kv_heads"]
+    attn = d * nh * hd + 2 * d * nkv * hd + nh * hd * d
+    per_layer_shared = attn + d * E + 2 * d
+    total = L * (E * 3 * d * f + per_layer_shared) + 2 * V * d + d
+    active = L * (k * 3 * d * f + per_layer_shared) + 2 * V * d + d
+    assert round(total / 1e9) == round(pc["total_params_about"] / 1e9), total
+    assert round(active / 1e9) == round(pc["active_params_about"] / 1e9), active
+    for name in ("decode", "prefill", "skewed", "stack"):
+        wl = inputs.WORKLOADS[name]
+        assert (wl.d, wl.f, wl.E, wl.k) == (d, f, E, k)
+    assert inputs.WORKLOADS["stack"].layers == L
+
+
+ALL_FAST_PINS = [
+    check_gate_invariants, check_k_distinct, check_brute_force, check_identical_experts,
+    check_special_k, check_all_ties, check_bias, check_invariances, check_silu,
+    check_forced, check_rmsnorm,
+]
