@@ -134,6 +134,22 @@ size_t moe_ffn_workspace_bytes(int64_t T, int64_t d, int64_t f, int64_t E, int64
 moe_status_t moe_rmsnorm(const void *h, void *x, int64_t T, int64_t d, float eps,
                          int32_t dtype, void *stream);
 
+/*
+ * Per-stage timing with HIP events, for benchmarks and tools.  Between
+ * moe_ffn_profile_begin and moe_ffn_profile_end, the first max_calls forward
+ * calls (any entry point, any stream) record an event at each stage boundary
+ * on their own stream.  moe_ffn_profile_end waits for those events and writes
+ * the summed milliseconds of each stage over the recorded calls into
+ * stage_ms[MOE_NUM_STAGES] and the number of recorded calls into *calls.
+ * Stages, in launch order: 0 router_topk, 1 route_scan, 2 gather_rows,
+ * 3 gemm1_swiglu, 4 gemm2, 5 sum_splits (0 ms unless y_out is asked for),
+ * 6 combine.  Not for concurrent use from several host threads.
+ */
+#define MOE_NUM_STAGES 7
+moe_status_t moe_ffn_profile_begin(int32_t max_calls);
+moe_status_t moe_ffn_profile_end(float *stage_ms, int32_t *calls);
+const char *moe_ffn_stage_name(int32_t stage);
+
 /* Text describing the last non-OK status returned on this host thread. */
 const char *moe_ffn_last_error(void);
 

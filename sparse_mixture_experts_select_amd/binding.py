@@ -1,0 +1,222 @@
+"""Thin ctypes binding of libmoe_ffn.so (``include/moe_ffn.h``).
+
+Same entry-point names as the C ABI.  The functions take torch tensors that
+live on the GPU, check their shapes and dtypes, and pass raw device pointers
+and the current HIP stream to the library; every step of the layer runs in
+the library's HIP kernels.  Importing this module loads the library and
+raises ``ImportError`` if it has not been built
+(``python -m sparse_mixture_experts_select_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libmoe_ffn.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_HIP = 3
+MOE_ERR_OUT_OF_MEMORY = 4
+MOE_DTYPE_BF16 = 0
+MOE_DTYPE_F32 = 1
+MOE_NUM_STAGES = 7
+
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
+                3: "MOE_ERR_HIP", 4: "MOE_ERR_OUT_OF_MEMORY"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libmoe_ffn.so is not built (expected at %s); run "
+                      "`python -m sparse_mixture_experts_select_amd.build`" % LIB_PATH)
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+class MoeFfnOpts(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("router_bias", _P),
+        ("topk_ids", _P),
+        ("topk_weights", _P),
+        ("expert_counts", _P),
+        ("expert_offsets", _P),
+        ("row_token", _P),
+        ("slot_row", _P),
+        ("h_out", _P),
+        ("y_out", _P),
+        ("residual", _P),
+        ("workspace", _P),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_FWD_ARGS = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P]
+lib.moe_ffn_forward.argtypes = _FWD_ARGS
+lib.moe_ffn_forward.restype = ctypes.c_int
+lib.moe_ffn_forward_f32.argtypes = _FWD_ARGS
+lib.moe_ffn_forward_f32.restype = ctypes.c_int
+lib.moe_ffn_forward_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(MoeFfnOpts)]
+lib.moe_ffn_forward_ex.restype = ctypes.c_int
+lib.moe_ffn_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int32]
+lib.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
+lib.moe_rmsnorm.argtypes = [_P, _P, _I64, _I64, ctypes.c_float, ctypes.c_int32, _P]
+lib.moe_rmsnorm.restype = ctypes.c_int
+lib.moe_ffn_last_error.argtypes = []
+lib.moe_ffn_last_error.restype = ctypes.c_char_p
+lib.moe_ffn_release_workspace.argtypes = []
+lib.moe_ffn_release_workspace.restype = None
+lib.moe_ffn_profile_begin.argtypes = [ctypes.c_int32]
+lib.moe_ffn_profile_begin.restype = ctypes.c_int
+lib.moe_ffn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
+lib.moe_ffn_profile_end.restype = ctypes.c_int
+lib.moe_ffn_stage_name.argtypes = [ctypes.c_int32]
+lib.moe_ffn_stage_name.restype = ctypes.c_char_p
+lib.moe_ffn_version.argtypes = []
+lib.moe_ffn_version.restype = ctypes.c_char_p
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, str(status)), message))
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, moe_ffn_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return MOE_DTYPE_BF16
+    if dt == torch.float32:
+        return MOE_DTYPE_F32
+    raise TypeError("tensors must be bfloat16 or float32, got %s" % dt)
+
+
+def _shapes(x, w_router, w1, w3, w2):
+    for name, t in (("x", x), ("w_router", w_router), ("w1", w1), ("w3", w3), ("w2", w2)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+    T, d = x.shape
+    E, d1, f = w1.shape
+    if w_router.shape != (d, E) or w3.shape != (E, d, f) or w2.shape != (E, f, d) or d1 != d:
+        raise ValueError("expected x [T,d], w_router [d,E], w1/w3 [E,d,f], w2 [E,f,d]; got %s %s %s %s %s"
+                         % (tuple(x.shape), tuple(w_router.shape), tuple(w1.shape), tuple(w3.shape),
+                            tuple(w2.shape)))
+    dts = {t.dtype for t in (x, w_router, w1, w3, w2)}
+    if len(dts) != 1:
+        raise TypeError("x and all weights must share one dtype")
+    return T, d, f, E
+
+
+def moe_ffn_forward(x, w_router, w1, w3, w2, k, out=None, stream=None):
+    """The layer in bfloat16 (fp32 accumulation); returns ``out`` [T,d]."""
+    T, d, f, E = _shapes(x, w_router, w1, w3, w2)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("moe_ffn_forward takes bfloat16 tensors")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib.moe_ffn_forward(_ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3), _ptr(w2),
+                               T, d, f, E, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_ffn_forward_f32(x, w_router, w1, w3, w2, k, out=None, stream=None):
+    """The layer in binary32; returns ``out`` [T,d]."""
+    T, d, f, E = _shapes(x, w_router, w1, w3, w2)
+    if x.dtype != torch.float32:
+        raise TypeError("moe_ffn_forward_f32 takes float32 tensors")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib.moe_ffn_forward_f32(_ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3), _ptr(w2),
+                                   T, d, f, E, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_ffn_forward_ex(x, w_router, w1, w3, w2, k, out=None, stream=None, *, router_bias=None,
+                       topk_ids=None, topk_weights=None, expert_counts=None, expert_offsets=None,
+                       row_token=None, slot_row=None, h_out=None, y_out=None, residual=None,
+                       workspace=None):
+    """The layer with options (see ``moe_ffn_opts_t``); every option is a GPU
+    tensor or None.  Returns ``out``."""
+    T, d, f, E = _shapes(x, w_router, w1, w3, w2)
+    if out is None:
+        out = torch.empty_like(x)
+    opts = MoeFfnOpts()
+    opts.dtype = _dtype_code(x.dtype)
+    opts.router_bias = None if router_bias is None else router_bias.data_ptr()
+    for name, t in (("topk_ids", topk_ids), ("topk_weights", topk_weights),
+                    ("expert_counts", expert_counts), ("expert_offsets", expert_offsets),
+                    ("row_token", row_token), ("slot_row", slot_row), ("h_out", h_out),
+                    ("y_out", y_out), ("residual", residual)):
+        if t is not None:
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous GPU tensor" % name)
+            setattr(opts, name, t.data_ptr())
+    if workspace is not None:
+        opts.workspace = workspace.data_ptr()
+        opts.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.moe_ffn_forward_ex(_ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3), _ptr(w2),
+                                  T, d, f, E, k, _ptr(out), _stream(stream), ctypes.byref(opts)))
+    return out
+
+
+def moe_ffn_workspace_bytes(T, d, f, E, k, dtype=MOE_DTYPE_BF16) -> int:
+    return int(lib.moe_ffn_workspace_bytes(T, d, f, E, k, dtype))
+
+
+def moe_rmsnorm(h, x=None, eps=1e-5, stream=None):
+    """Unit-gain RMSNorm of each row of h [T,d]; returns x."""
+    if not h.is_cuda or not h.is_contiguous():
+        raise ValueError("h must be a contiguous GPU tensor")
+    if x is None:
+        x = torch.empty_like(h)
+    T, d = h.shape
+    _check(lib.moe_rmsnorm(_ptr(h), _ptr(x), T, d, float(eps), _dtype_code(h.dtype), _stream(stream)))
+    return x
+
+
+def moe_ffn_last_error() -> str:
+    return lib.moe_ffn_last_error().decode()
+
+
+def moe_ffn_release_workspace() -> None:
+    lib.moe_ffn_release_workspace()
+
+
+def moe_ffn_version() -> str:
+    return lib.moe_ffn_version().decode()
+
+
+def moe_ffn_profile_begin(max_calls: int) -> None:
+    _check(lib.moe_ffn_profile_begin(max_calls))
+
+
+def moe_ffn_profile_end():
+    """Returns ({stage name: summed ms}, number of recorded calls)."""
+    ms = (ctypes.c_float * MOE_NUM_STAGES)()
+    calls = ctypes.c_int32(0)
+    _check(lib.moe_ffn_profile_end(ms, ctypes.byref(calls)))
+    return {moe_ffn_stage_name(i): float(ms[i]) for i in range(MOE_NUM_STAGES)}, int(calls.value)
+
+
+def moe_ffn_stage_name(i: int) -> str:
+    return lib.moe_ffn_stage_name(i).decode()

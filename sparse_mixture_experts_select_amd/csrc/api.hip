@@ -1,0 +1,377 @@
+// api.hip -- the C ABI of libmoe_ffn: argument validation, workspace, and the
+// launch sequence of the layer on one stream.
+//
+// Mixtral of Experts (wikillm.com card, "Method"): router, top-k with a
+// softmax over the kept logits, SwiGLU experts, gate-weighted sum (section
+// 2.1 displays 1-3), applied to a whole batch grouped by expert.  One call
+// enqueues, in stream order:
+//   1. router_topk    x, w_router        -> ids [T,k], gates [T,k]
+//   2. route_scan     ids                -> counts, offsets, slot_row, row_token
+//   3. gather_rows    x, row_token       -> x_perm [T*k, d]
+//   4. gemm1_swiglu   x_perm, w1, w3     -> h [T*k, f]
+//   5. gemm2          h, w2              -> y [splits][T*k, d] (fp32)
+//   6. combine        y, gates, slot_row -> out [T,d] (+ residual)
+// Nothing is read back to the host, so the host never waits for the GPU
+// (except when the cached workspace has to grow).
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+#include "moe_ffn.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* where) {
+    return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+struct Plan {
+    int variant = GEMM_LARGE_M;
+    int splits = 1;
+    size_t ids = 0, gates = 0, counts = 0, offsets = 0, slot_row = 0, row_token = 0;
+    size_t x_perm = 0, h = 0, y = 0, total = 0;
+};
+
+// Tile variant and K-split of the bf16 GEMMs, and the workspace layout.
+Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype) {
+    Plan p;
+    const int64_t R = T * k;
+    const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
+    if (dtype == MOE_DTYPE_BF16) {
+        // Few rows per expert: 32-row tiles; otherwise 128-row tiles.
+        p.variant = (R <= 64 * E) ? GEMM_SMALL_M : GEMM_LARGE_M;
+        const int64_t bm = gemm_bm(p.variant);
+        const int64_t nt2 = (d + gemm2_bn(p.variant) - 1) / gemm2_bn(p.variant);
+        const int64_t busy_experts = R < E ? R : E;
+        int64_t mt = (R + bm - 1) / bm;
+        if (mt < busy_experts) mt = busy_experts;
+        const int64_t tiles = nt2 * mt;
+        // Cut the w2 contraction when GEMM 2 alone would not give every CU
+        // a couple of workgroups; keep at least 4 K steps per slice.
+        int64_t s = (512 + tiles - 1) / tiles;
+        const int64_t kt = f / 64;
+        int64_t smax = kt / 4 < 8 ? kt / 4 : 8;
+        if (smax < 1) smax = 1;
+        if (s > smax) s = smax;
+        if (s < 1) s = 1;
+        p.splits = (int)s;
+    }
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    p.ids = take((size_t)R * 4);
+    p.gates = take((size_t)R * 4);
+    p.counts = take((size_t)E * 4);
+    p.offsets = take((size_t)(E + 1) * 4);
+    p.slot_row = take((size_t)R * 4);
+    p.row_token = take((size_t)R * 4);
+    p.x_perm = take((size_t)R * d * es);
+    p.h = take((size_t)R * f * es);
+    p.y = take((size_t)p.splits * R * d * 4);
+    p.total = off;
+    return p;
+}
+
+moe_status_t check_sizes(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype) {
+    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32)
+        return fail(MOE_ERR_INVALID_ARG, "dtype %d is neither MOE_DTYPE_BF16 nor MOE_DTYPE_F32", dtype);
+    if (T < 0 || d < 1 || f < 1 || E < 1 || k < 1)
+        return fail(MOE_ERR_INVALID_ARG, "sizes must be T >= 0 and d, f, E, k >= 1 (got T=%lld d=%lld f=%lld E=%lld k=%lld)",
+                    (long long)T, (long long)d, (long long)f, (long long)E, (long long)k);
+    if (k > E) return fail(MOE_ERR_UNSUPPORTED, "k=%lld exceeds E=%lld", (long long)k, (long long)E);
+    if (E > 64) return fail(MOE_ERR_UNSUPPORTED, "E=%lld exceeds 64", (long long)E);
+    if (k > 8) return fail(MOE_ERR_UNSUPPORTED, "k=%lld exceeds 8", (long long)k);
+    const int64_t mult = dtype == MOE_DTYPE_BF16 ? 64 : 4;
+    if (d % mult != 0 || f % mult != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "d=%lld and f=%lld must be multiples of %lld", (long long)d,
+                    (long long)f, (long long)mult);
+    const int64_t lim = (int64_t)1 << 30;
+    if (T * k >= lim || d >= lim || f >= lim)
+        return fail(MOE_ERR_UNSUPPORTED, "T*k, d and f must each be below 2^30");
+    return MOE_OK;
+}
+
+struct WorkspaceCache {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+WorkspaceCache g_ws[64];
+
+moe_status_t cached_workspace(size_t need, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d >= 64", dev);
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    WorkspaceCache& c = g_ws[dev];
+    if (c.bytes < need) {
+        if (c.ptr != nullptr) {
+            // Work already enqueued may still use the old buffer.
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            e = hipFree(c.ptr);
+            c.ptr = nullptr;
+            c.bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+        }
+        void* p = nullptr;
+        e = hipMalloc(&p, need);
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return fail(MOE_ERR_OUT_OF_MEMORY, "hipMalloc of %zu workspace bytes failed: %s", need,
+                        hipGetErrorString(e));
+        }
+        c.ptr = p;
+        c.bytes = need;
+    }
+    *out = c.ptr;
+    return MOE_OK;
+}
+
+// Stage-boundary events of profiled calls (moe_ffn_profile_begin/end).
+struct Profiler {
+    bool active = false;
+    int max_calls = 0;
+    int calls = 0;
+    hipEvent_t* ev = nullptr;  // [max_calls][MOE_NUM_STAGES + 1]
+};
+std::mutex g_prof_mu;
+Profiler g_prof;
+
+// Events for the next profiled call, or nullptr.
+hipEvent_t* profile_slot() {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof.active || g_prof.calls >= g_prof.max_calls) return nullptr;
+    return g_prof.ev + (size_t)(g_prof.calls++) * (MOE_NUM_STAGES + 1);
+}
+
+#define LAUNCH(call, name)                                   \
+    do {                                                     \
+        hipError_t e_ = (call);                              \
+        if (e_ != hipSuccess) return hip_fail(e_, name);     \
+    } while (0)
+
+moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, const void* w3,
+                          const void* w2, int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
+                          void* out, void* stream_ptr, const moe_ffn_opts_t* opts, int dtype) {
+    moe_status_t st = check_sizes(T, d, f, E, k, dtype);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !w1 || !w3 || !w2 || !out)
+        return fail(MOE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    const void* must_align[] = {x, w_router, w1, w3, w2, out,
+                                opts ? opts->residual : nullptr,
+                                opts ? opts->h_out : nullptr,
+                                opts ? (const void*)opts->y_out : nullptr,
+                                opts ? opts->workspace : nullptr};
+    for (const void* p : must_align)
+        if (p && !aligned16(p)) return fail(MOE_ERR_UNSUPPORTED, "a tensor pointer is not 16-byte aligned");
+
+    const Plan plan = make_plan(T, d, f, E, k, dtype);
+    char* ws = nullptr;
+    if (opts && opts->workspace) {
+        if (opts->workspace_bytes < plan.total)
+            return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu needed",
+                        opts->workspace_bytes, plan.total);
+        ws = static_cast<char*>(opts->workspace);
+    } else {
+        void* p = nullptr;
+        st = cached_workspace(plan.total, &p);
+        if (st != MOE_OK) return st;
+        ws = static_cast<char*>(p);
+    }
+
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+    const int Ti = (int)T, di = (int)d, fi = (int)f, Ei = (int)E, ki = (int)k;
+    const int R = Ti * ki;
+    int32_t* ids = (opts && opts->topk_ids) ? opts->topk_ids : reinterpret_cast<int32_t*>(ws + plan.ids);
+    float* gates = (opts && opts->topk_weights) ? opts->topk_weights : reinterpret_cast<float*>(ws + plan.gates);
+    int32_t* counts = (opts && opts->expert_counts) ? opts->expert_counts : reinterpret_cast<int32_t*>(ws + plan.counts);
+    int32_t* offsets = (opts && opts->expert_offsets) ? opts->expert_offsets : reinterpret_cast<int32_t*>(ws + plan.offsets);
+    int32_t* slot_row = (opts && opts->slot_row) ? opts->slot_row : reinterpret_cast<int32_t*>(ws + plan.slot_row);
+    int32_t* row_token = (opts && opts->row_token) ? opts->row_token : reinterpret_cast<int32_t*>(ws + plan.row_token);
+    void* x_perm = ws + plan.x_perm;
+    void* h = (opts && opts->h_out) ? opts->h_out : (void*)(ws + plan.h);
+    float* y = reinterpret_cast<float*>(ws + plan.y);
+    const float* bias = opts ? opts->router_bias : nullptr;
+    const void* residual = opts ? opts->residual : nullptr;
+
+    hipEvent_t* ev = profile_slot();
+    auto mark = [&](int i) {
+        if (ev) (void)hipEventRecord(ev[i], stream);
+    };
+    mark(0);
+    LAUNCH(launch_router_topk(dtype, x, w_router, bias, Ti, di, Ei, ki, ids, gates, stream), "router_topk");
+    mark(1);
+    LAUNCH(launch_route_scan(ids, Ti, ki, Ei, counts, offsets, slot_row, row_token, stream), "route_scan");
+    mark(2);
+    LAUNCH(launch_gather_rows(dtype, x, row_token, R, di, x_perm, stream), "gather_rows");
+    mark(3);
+    if (dtype == MOE_DTYPE_BF16) {
+        LAUNCH(launch_gemm1_swiglu_bf16(plan.variant, x_perm, w1, w3, offsets, R, Ei, di, fi, h, stream), "gemm1_swiglu");
+        mark(4);
+        LAUNCH(launch_gemm2_bf16(plan.variant, h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");
+    } else {
+        LAUNCH(launch_gemm1_swiglu_f32(x_perm, w1, w3, offsets, R, Ei, di, fi, h, stream), "gemm1_swiglu");
+        mark(4);
+        LAUNCH(launch_gemm2_f32(h, w2, offsets, R, Ei, fi, di, y, stream), "gemm2");
+    }
+    mark(5);
+    if (opts && opts->y_out)
+        LAUNCH(launch_sum_splits(y, plan.splits, R, di, opts->y_out, stream), "sum_splits");
+    mark(6);
+    LAUNCH(launch_combine(dtype, y, plan.splits, gates, slot_row, residual, Ti, di, ki, R, out, stream), "combine");
+    mark(7);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_ffn_forward(const void* x, const void* w_router, const void* w1, const void* w3,
+                             const void* w2, int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
+                             void* out, void* stream) {
+    return forward_impl(x, w_router, w1, w3, w2, T, d, f, E, k, out, stream, nullptr, MOE_DTYPE_BF16);
+}
+
+moe_status_t moe_ffn_forward_f32(const float* x, const float* w_router, const float* w1,
+                                 const float* w3, const float* w2, int64_t T, int64_t d, int64_t f,
+                                 int64_t E, int64_t k, float* out, void* stream) {
+    return forward_impl(x, w_router, w1, w3, w2, T, d, f, E, k, out, stream, nullptr, MOE_DTYPE_F32);
+}
+
+moe_status_t moe_ffn_forward_ex(const void* x, const void* w_router, const void* w1,
+                                const void* w3, const void* w2, int64_t T, int64_t d, int64_t f,
+                                int64_t E, int64_t k, void* out, void* stream,
+                                const moe_ffn_opts_t* opts) {
+    const int dtype = opts ? opts->dtype : MOE_DTYPE_BF16;
+    return forward_impl(x, w_router, w1, w3, w2, T, d, f, E, k, out, stream, opts, dtype);
+}
+
+size_t moe_ffn_workspace_bytes(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int32_t dtype) {
+    char saved[sizeof g_err];
+    memcpy(saved, g_err, sizeof g_err);
+    const moe_status_t st = check_sizes(T, d, f, E, k, dtype);
+    memcpy(g_err, saved, sizeof g_err);
+    if (st != MOE_OK) return 0;
+    return make_plan(T, d, f, E, k, dtype).total;
+}
+
+moe_status_t moe_rmsnorm(const void* h, void* x, int64_t T, int64_t d, float eps, int32_t dtype,
+                         void* stream) {
+    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32)
+        return fail(MOE_ERR_INVALID_ARG, "dtype %d is neither MOE_DTYPE_BF16 nor MOE_DTYPE_F32", dtype);
+    if (T < 0 || d < 1 || !(eps >= 0.0f))
+        return fail(MOE_ERR_INVALID_ARG, "need T >= 0, d >= 1, eps >= 0");
+    const int64_t mult = dtype == MOE_DTYPE_BF16 ? 8 : 4;
+    if (d % mult != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "d=%lld must be a multiple of %lld", (long long)d, (long long)mult);
+    if (T >= ((int64_t)1 << 30) || d >= ((int64_t)1 << 30))
+        return fail(MOE_ERR_UNSUPPORTED, "T and d must be below 2^30");
+    if (T == 0) return MOE_OK;
+    if (!h || !x) return fail(MOE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    if (!aligned16(h) || !aligned16(x)) return fail(MOE_ERR_UNSUPPORTED, "a tensor pointer is not 16-byte aligned");
+    LAUNCH(launch_rmsnorm(dtype, h, x, (int)T, (int)d, eps, reinterpret_cast<hipStream_t>(stream)), "rmsnorm");
+    return MOE_OK;
+}
+
+moe_status_t moe_ffn_profile_begin(int32_t max_calls) {
+    if (max_calls < 1 || max_calls > 1000000)
+        return fail(MOE_ERR_INVALID_ARG, "max_calls must be in [1, 1e6]");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof.active) return fail(MOE_ERR_INVALID_ARG, "profiling already active");
+    const size_t n = (size_t)max_calls * (MOE_NUM_STAGES + 1);
+    hipEvent_t* ev = new hipEvent_t[n];
+    for (size_t i = 0; i < n; ++i) {
+        const hipError_t e = hipEventCreate(&ev[i]);
+        if (e != hipSuccess) {
+            for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+            delete[] ev;
+            return hip_fail(e, "hipEventCreate");
+        }
+    }
+    g_prof.ev = ev;
+    g_prof.max_calls = max_calls;
+    g_prof.calls = 0;
+    g_prof.active = true;
+    return MOE_OK;
+}
+
+moe_status_t moe_ffn_profile_end(float* stage_ms, int32_t* calls) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof.active) return fail(MOE_ERR_INVALID_ARG, "profiling is not active");
+    moe_status_t st = MOE_OK;
+    float sums[MOE_NUM_STAGES] = {0};
+    for (int c = 0; c < g_prof.calls && st == MOE_OK; ++c) {
+        hipEvent_t* e = g_prof.ev + (size_t)c * (MOE_NUM_STAGES + 1);
+        hipError_t r = hipEventSynchronize(e[MOE_NUM_STAGES]);
+        if (r != hipSuccess) { st = hip_fail(r, "hipEventSynchronize"); break; }
+        for (int s = 0; s < MOE_NUM_STAGES; ++s) {
+            float ms = 0.0f;
+            r = hipEventElapsedTime(&ms, e[s], e[s + 1]);
+            if (r != hipSuccess) { st = hip_fail(r, "hipEventElapsedTime"); break; }
+            sums[s] += ms;
+        }
+    }
+    const size_t n = (size_t)g_prof.max_calls * (MOE_NUM_STAGES + 1);
+    for (size_t i = 0; i < n; ++i) (void)hipEventDestroy(g_prof.ev[i]);
+    delete[] g_prof.ev;
+    const int recorded = g_prof.calls;
+    g_prof = Profiler();
+    if (st != MOE_OK) return st;
+    if (stage_ms) for (int s = 0; s < MOE_NUM_STAGES; ++s) stage_ms[s] = sums[s];
+    if (calls) *calls = recorded;
+    return MOE_OK;
+}
+
+const char* moe_ffn_stage_name(int32_t stage) {
+    static const char* names[MOE_NUM_STAGES] = {"router_topk", "route_scan", "gather_rows",
+                                                "gemm1_swiglu", "gemm2", "sum_splits", "combine"};
+    return (stage >= 0 && stage < MOE_NUM_STAGES) ? names[stage] : "";
+}
+
+const char* moe_ffn_last_error(void) { return g_err; }
+
+void moe_ffn_release_workspace(void) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (int dev = 0; dev < 64; ++dev) {
+        WorkspaceCache& c = g_ws[dev];
+        if (c.ptr == nullptr) continue;
+        if (hipSetDevice(dev) == hipSuccess) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(c.ptr);
+        }
+        c.ptr = nullptr;
+        c.bytes = 0;
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+}
+
+const char* moe_ffn_version(void) { return "0.1.0"; }
+
+}  // extern "C"

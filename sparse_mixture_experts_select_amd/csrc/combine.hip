@@ -1,0 +1,132 @@
+// combine.hip -- gate-weighted un-permute of the expert outputs, and RMSNorm.
+//
+// Mixtral of Experts (wikillm.com card, "Method"): the token's output is the
+// sum over its k kept experts of gate * expert output, starting from zero
+// (section 2.1 displays 1 and 3, moe_feed_forward pseudocode).  The expert
+// outputs sit in grouped-row order; slot_row maps token t's j-th pick to its
+// row.  Sums run in fp32 in a fixed order (K-split partials first, then picks
+// j = 0..k-1), so results are bitwise reproducible.  With a residual the sum
+// is residual + layer output, rounded once to the storage type.
+//
+// RMSNorm (unit gain) serves the stacked form h = h + MoE(RMSNorm(h)); the
+// pages leave the normalisation to the code ("Method", steps for one token,
+// item 5).  One workgroup per row, fp32 sum of squares, one rounding.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <typename T> struct Io;
+template <> struct Io<bf16> {
+    __device__ static void load4(const void* p, size_t i, float* v) {
+        const uint2 q = reinterpret_cast<const uint2*>(p)[i];
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+    }
+    __device__ static void store4(void* p, size_t i, const float* v) {
+        uint2 q;
+        q.x = pack_bf16x2(v[0], v[1]);
+        q.y = pack_bf16x2(v[2], v[3]);
+        reinterpret_cast<uint2*>(p)[i] = q;
+    }
+};
+template <> struct Io<float> {
+    __device__ static void load4(const void* p, size_t i, float* v) {
+        const float4 q = reinterpret_cast<const float4*>(p)[i];
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+    __device__ static void store4(void* p, size_t i, const float* v) {
+        reinterpret_cast<float4*>(p)[i] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int splits,
+                                                      size_t split_stride,
+                                                      const float* __restrict__ gates,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const void* residual, int Tn, int d, int k,
+                                                      void* out) {
+    const int d4 = d / 4;
+    for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
+        for (int c = threadIdx.x; c < d4; c += 256) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < k; ++j) {
+                const int r = slot_row[(size_t)t * k + j];
+                const float g = gates[(size_t)t * k + j];
+                const float4* yr = reinterpret_cast<const float4*>(y + (size_t)r * d);
+                float4 s = yr[c];
+                for (int p = 1; p < splits; ++p) {
+                    const float4 v =
+                        reinterpret_cast<const float4*>(y + p * split_stride + (size_t)r * d)[c];
+                    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+                }
+                acc[0] += g * s.x; acc[1] += g * s.y; acc[2] += g * s.z; acc[3] += g * s.w;
+            }
+            const size_t idx = (size_t)t * d4 + c;
+            if (residual != nullptr) {
+                float rv[4];
+                Io<T>::load4(residual, idx, rv);
+                for (int u = 0; u < 4; ++u) acc[u] = rv[u] + acc[u];
+            }
+            Io<T>::store4(out, idx, acc);
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void* h, void* x, int Tn, int d,
+                                                      float eps) {
+    __shared__ float part[4];
+    const int d4 = d / 4;
+    for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
+        float ss = 0.0f;
+        for (int c = threadIdx.x; c < d4; c += 256) {
+            float v[4];
+            Io<T>::load4(h, (size_t)t * d4 + c, v);
+            ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        }
+        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+        __syncthreads();
+        const float tot = part[0] + part[1] + part[2] + part[3];
+        const float r = 1.0f / sqrtf(tot / (float)d + eps);
+        for (int c = threadIdx.x; c < d4; c += 256) {
+            float v[4];
+            Io<T>::load4(h, (size_t)t * d4 + c, v);
+            for (int u = 0; u < 4; ++u) v[u] *= r;
+            Io<T>::store4(x, (size_t)t * d4 + c, v);
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const float* y, int splits, const float* gates,
+                          const int32_t* slot_row, const void* residual, int T, int d, int k, int R,
+                          void* out, hipStream_t stream) {
+    int blocks = T < 16384 ? T : 16384;
+    if (blocks < 1) blocks = 1;
+    const size_t split_stride = (size_t)R * d;
+    if (dtype == 0)
+        hipLaunchKernelGGL(combine_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, y, splits,
+                           split_stride, gates, slot_row, residual, T, d, k, out);
+    else
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, y, splits,
+                           split_stride, gates, slot_row, residual, T, d, k, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int dtype, const void* h, void* x, int T, int d, float eps,
+                          hipStream_t stream) {
+    int blocks = T < 16384 ? T : 16384;
+    if (blocks < 1) blocks = 1;
+    if (dtype == 0)
+        hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, h, x, T, d, eps);
+    else
+        hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(blocks), dim3(256), 0, stream, h, x, T, d,
+                           eps);
+    return hipGetLastError();
+}
+
+}  // namespace moe

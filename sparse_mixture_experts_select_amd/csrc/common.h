@@ -1,0 +1,80 @@
+// common.h -- device types, conversions and launcher declarations shared by
+// the kernels of libmoe_ffn (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Widening bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// SiLU(z) = z * sigmoid(z), fp32.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// Kernel launchers.  Each returns the hipGetLastError() of its launch(es).
+// dtype: 0 = bf16, 1 = fp32 (same codes as moe_dtype_t).
+
+hipError_t launch_router_topk(int dtype, const void* x, const void* w_router, const float* bias,
+                              int T, int d, int E, int k, int32_t* ids, float* gates,
+                              hipStream_t stream);
+
+hipError_t launch_route_scan(const int32_t* ids, int T, int k, int E, int32_t* counts,
+                             int32_t* offsets, int32_t* slot_row, int32_t* row_token,
+                             hipStream_t stream);
+
+hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token, int R, int d,
+                              void* x_perm, hipStream_t stream);
+
+// Grouped GEMM 1 with the SwiGLU epilogue: for each grouped row r of expert e,
+// h[r,:] = SiLU(x_perm[r,:] . w1[e]) * (x_perm[r,:] . w3[e]).
+hipError_t launch_gemm1_swiglu_bf16(int variant, const void* x_perm, const void* w1,
+                                    const void* w3, const int32_t* offsets, int R, int E, int d,
+                                    int f, void* h, hipStream_t stream);
+hipError_t launch_gemm1_swiglu_f32(const void* x_perm, const void* w1, const void* w3,
+                                   const int32_t* offsets, int R, int E, int d, int f, void* h,
+                                   hipStream_t stream);
+
+// Grouped GEMM 2: y[s][r,:] = h[r, Ks] . w2[e][Ks, :] over the s-th of
+// `splits` equal slices Ks of the contraction; fp32 partials.
+hipError_t launch_gemm2_bf16(int variant, const void* h, const void* w2, const int32_t* offsets,
+                             int R, int E, int f, int d, int splits, float* y,
+                             hipStream_t stream);
+hipError_t launch_gemm2_f32(const void* h, const void* w2, const int32_t* offsets, int R, int E,
+                            int f, int d, float* y, hipStream_t stream);
+
+// out[t,:] = (residual[t,:] +) sum_j gates[t,j] * sum_s y[s][slot_row[t*k+j], :]
+hipError_t launch_combine(int dtype, const float* y, int splits, const float* gates,
+                          const int32_t* slot_row, const void* residual, int T, int d, int k, int R,
+                          void* out, hipStream_t stream);
+
+// y_out[r,:] = sum_s y[s][r,:]
+hipError_t launch_sum_splits(const float* y, int splits, int R, int d, float* y_out,
+                             hipStream_t stream);
+
+hipError_t launch_rmsnorm(int dtype, const void* h, void* x, int T, int d, float eps,
+                          hipStream_t stream);
+
+// Tile shapes of the bf16 grouped GEMMs, chosen by the host per call.
+enum GemmVariant { GEMM_LARGE_M = 0, GEMM_SMALL_M = 1 };
+int gemm_bm(int variant);      // rows per tile
+int gemm1_bn(int variant);     // h columns per tile
+int gemm2_bn(int variant);     // y columns per tile
+
+}  // namespace moe

@@ -108,10 +108,10 @@ def make_x(T, d, dtype, device, x_dist="normal", seed=0, workload="case", rms_ep
     g = torch.Generator(device=device)
     g.manual_seed(tensor_seed(seed, workload, 0, "x"))
     z = torch.randn((T, d), generator=g, device=device, dtype=torch.float32)
+    if x_dist not in ("normal", "rms"):
+        raise ValueError(x_dist)
     if x_dist == "rms" and T > 0:
         z = z * torch.rsqrt(z.pow(2).mean(dim=1, keepdim=True) + rms_eps)
-    elif x_dist != "normal":
-        raise ValueError(x_dist)
     return z.to(dtype)
 
 

@@ -1,0 +1,180 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases compare every output element; the full-size workloads check
+routing on every token and outputs (plus the SwiGLU activations h and the
+expert outputs y) on sampled tokens, in the same launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity as PT
+from sparse_mixture_experts_select_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def case(T, d, f, E, dtype, seed, x_dist="rms", bias=None, label="case"):
+    inp = inputs.make_weights(d, f, E, dtype, DEV, seed, label)
+    inp["x"] = inputs.make_x(T, d, dtype, DEV, x_dist, seed, label)
+    inp["bias"] = None if bias is None else torch.tensor(bias, dtype=torch.float32, device=DEV)
+    return inp
+
+
+def banner(msg):
+    print("\n[case] " + msg, flush=True)
+
+
+def test_tiny_fp32_workload():
+    banner("tiny fp32 T=64 d=128 f=256 E=8 k=2")
+    inp = inputs.workload_inputs("tiny", DEV)
+    r = PT.full_check(inp, 2, label="tiny")
+    print(r["label"], "near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
+
+
+SMALL = [
+    # T, d, f, E, k, dtype
+    (300, 192, 320, 8, 2, torch.bfloat16),    # 128-row tiles, ragged rows and columns
+    (40, 256, 384, 8, 2, torch.bfloat16),     # 32-row tiles
+    (1, 128, 128, 8, 2, torch.bfloat16),      # one token
+    (257, 512, 640, 6, 3, torch.bfloat16),
+    (100, 128, 192, 4, 1, torch.bfloat16),    # k = 1
+    (64, 128, 128, 4, 4, torch.bfloat16),     # k = E: dense softmax mixture
+    (33, 64, 128, 1, 1, torch.bfloat16),      # E = 1: plain SwiGLU
+    (100, 128, 128, 64, 8, torch.bfloat16),   # widest routing
+    (700, 256, 256, 8, 2, torch.bfloat16),    # several 128-row tiles per expert
+    (50, 100, 60, 5, 2, torch.float32),
+    (200, 64, 96, 16, 4, torch.float32),
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,k,dtype", SMALL)
+def test_small_shapes(T, d, f, E, k, dtype):
+    banner("small T=%d d=%d f=%d E=%d k=%d %s" % (T, d, f, E, k, dtype))
+    inp = case(T, d, f, E, dtype, seed=T + d + f + E + k, label="small")
+    r = PT.full_check(inp, k)
+    print("near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
+
+
+def test_all_logits_tied():
+    banner("w_router = 0")
+    inp = case(70, 128, 128, 8, torch.bfloat16, seed=5, label="ties")
+    inp["w_router"].zero_()
+    g = PT.run_gpu(inp, 2)
+    ids = PT.to_np(g["ids"])
+    assert np.all(ids[:, 0] == 0) and np.all(ids[:, 1] == 1)
+    assert np.all(PT.to_np(g["gates"]) == 0.5)
+    np.testing.assert_array_equal(PT.to_np(g["counts"]), [70, 70, 0, 0, 0, 0, 0, 0])
+    host = PT.host_inputs(inp)
+    ref_g = np.full((70, 2), 0.5)
+    PT.check_outputs(g, host, np.arange(70), ref_g, 2, torch.bfloat16)
+
+
+def test_imbalanced_and_empty_experts():
+    banner("bias: expert 3 takes every token, experts 5-7 get none")
+    bias = [0.0, 0.0, 0.0, 40.0, 0.0, -40.0, -40.0, -40.0]
+    inp = case(300, 256, 256, 8, torch.bfloat16, seed=6, bias=bias, label="skew")
+    r = PT.full_check(inp, 2)
+    counts = PT.to_np(r["gpu"]["counts"])
+    assert counts[3] == 300 and counts[5:].sum() == 0
+
+
+def test_zero_tokens_leaves_out_untouched():
+    from sparse_mixture_experts_select_amd import binding
+    inp = case(0, 128, 128, 8, torch.bfloat16, seed=1, label="empty")
+    out = torch.empty((0, 128), dtype=torch.bfloat16, device=DEV)
+    binding.moe_ffn_forward(inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], 2, out=out)
+    torch.cuda.synchronize()
+
+
+def test_forward_entry_points_agree_and_are_deterministic():
+    from sparse_mixture_experts_select_amd import binding
+    banner("determinism T=1000 d=256 f=512")
+    inp = case(1000, 256, 512, 8, torch.bfloat16, seed=7, label="det")
+    a = binding.moe_ffn_forward(inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], 2)
+    b = binding.moe_ffn_forward(inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], 2)
+    c = binding.moe_ffn_forward_ex(inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], 2)
+    nbytes = binding.moe_ffn_workspace_bytes(1000, 256, 512, 8, 2)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    dws = binding.moe_ffn_forward_ex(inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], 2,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), dws.view(torch.int16))
+
+
+def test_residual_and_in_place():
+    from sparse_mixture_experts_select_amd import binding
+    banner("residual")
+    inp = case(150, 128, 256, 8, torch.bfloat16, seed=8, label="res")
+    resid = inputs.make_x(150, 128, torch.bfloat16, DEV, "normal", 9, "resid")
+    plain = binding.moe_ffn_forward(inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], 2)
+    out = resid.clone()
+    binding.moe_ffn_forward_ex(inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"], 2,
+                               out=out, residual=out)
+    torch.cuda.synchronize()
+    want = (resid.float() + plain.float())
+    # residual + layer is rounded once; layer alone is rounded once too, so the
+    # two paths differ by at most one bf16 rounding of the layer output.
+    err = (out.float() - want).abs().max().item()
+    assert err <= 2 ** -7 * want.abs().max().item()
+    g = PT.run_gpu(inp, 2, residual=resid)
+    host = PT.host_inputs(inp)
+    logits, o_ids, _ = oracle.route(host["x"], host["w_router"], 2)
+    _, ref_g = PT.check_routing(g, logits, o_ids, 2)
+    PT.check_outputs(g, host, np.arange(150), ref_g, 2, torch.bfloat16,
+                     residual=PT.out_f64(resid))
+    # out == x is allowed
+    x2 = inp["x"].clone()
+    binding.moe_ffn_forward(x2, inp["w_router"], inp["w1"], inp["w3"], inp["w2"], 2, out=x2)
+    torch.cuda.synchronize()
+    assert torch.equal(x2.view(torch.int16), plain.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rmsnorm(dtype):
+    from sparse_mixture_experts_select_amd import binding
+    h = inputs.make_x(333, 4096 if dtype == torch.bfloat16 else 200, dtype, DEV, "normal", 3, "rms") * 3
+    x = binding.moe_rmsnorm(h, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(inputs.host_array(h), 1e-5)
+    got = PT.out_f64(x)
+    tol = 2 ** -8 if dtype == torch.bfloat16 else 1e-6
+    assert np.abs(got - ref).max() <= tol * np.abs(ref).max()
+
+
+# ---------------------------------------------------------------- workloads
+
+
+def sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(T, size=min(n, T), replace=False))
+
+
+def test_decode_workload():
+    banner("decode bf16 T=32 d=4096 f=14336 E=8 k=2 (all tokens)")
+    inp = inputs.workload_inputs("decode", DEV)
+    r = PT.full_check(inp, 2, label="decode")
+    print("near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
+
+
+def test_prefill_workload():
+    banner("prefill bf16 T=4096 (routing on all tokens, outputs on 24)")
+    inp = inputs.workload_inputs("prefill", DEV)
+    r = PT.full_check(inp, 2, tokens=sample_tokens(4096, 24, 1), label="prefill")
+    print("near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
+
+
+def test_skewed_workload():
+    banner("skewed bf16 T=16384 (routing on all tokens, outputs on 16)")
+    inp = inputs.workload_inputs("skewed", DEV)
+    r = PT.full_check(inp, 2, tokens=sample_tokens(16384, 16, 2), want_h=False, label="skewed")
+    counts = PT.to_np(r["gpu"]["counts"])
+    share = counts / counts.sum()
+    print("near ties", r["near_ties"], "err", r["err_out"], "shares", np.round(share, 3))
+    assert 0.35 < share[0] < 0.48
