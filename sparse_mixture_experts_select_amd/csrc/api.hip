@@ -56,23 +56,50 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
     const int64_t R = T * k;
     const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
     if (dtype == MOE_DTYPE_BF16) {
-        // Few rows per expert: 32-row tiles; otherwise 128-row tiles.
-        p.variant = (R <= 64 * E) ? GEMM_SMALL_M : GEMM_LARGE_M;
-        const int64_t bm = gemm_bm(p.variant);
-        const int64_t nt2 = (d + gemm2_bn(p.variant) - 1) / gemm2_bn(p.variant);
         const int64_t busy_experts = R < E ? R : E;
-        int64_t mt = (R + bm - 1) / bm;
-        if (mt < busy_experts) mt = busy_experts;
-        const int64_t tiles = nt2 * mt;
-        // Cut the w2 contraction when GEMM 2 alone would not give every CU
-        // a couple of workgroups; keep at least 4 K steps per slice.
-        int64_t s = (512 + tiles - 1) / tiles;
-        const int64_t kt = f / 64;
-        int64_t smax = kt / 4 < 8 ? kt / 4 : 8;
-        if (smax < 1) smax = 1;
-        if (s > smax) s = smax;
-        if (s < 1) s = 1;
-        p.splits = (int)s;
+        if (R <= 12 * E) {
+            // About a dozen rows or fewer per expert: stream the weights.
+            p.variant = GEMM_STREAM;
+            const int64_t nt2 = (d + 127) / 128;
+            int64_t mt = (R + 15) / 16;
+            if (mt < busy_experts) mt = busy_experts;
+            const int64_t tiles = nt2 * mt;
+            // GEMM 2 runs one slab per workgroup with the K range split over
+            // its 4 waves; cut K further across workgroups only when that
+            // leaves fewer than ~1000 waves streaming.
+            int64_t s = (256 + tiles - 1) / tiles;
+            int64_t smax = f / 128;
+            if (smax > 16) smax = 16;
+            if (smax < 1) smax = 1;
+            if (s > smax) s = smax;
+            if (s < 1) s = 1;
+            p.splits = (int)s;
+        } else if (R >= 128 * E) {
+            // Many rows per expert: 256x256 macro tiles.  GEMM 2 has d/256
+            // column tiles; when that gives under ~4 workgroups per CU, cut
+            // its K range in two (partials summed by the combine).
+            p.variant = GEMM_TILE256;
+            const int64_t nt2 = (d + 255) / 256;
+            const int64_t tiles = nt2 * ((R + 255) / 256 + E / 2);
+            p.splits = (tiles < 1024 && f / 64 >= 16) ? 2 : 1;
+        } else {
+            // Few rows per expert: 32-row tiles; otherwise 128-row tiles.
+            p.variant = (R <= 64 * E) ? GEMM_SMALL_M : GEMM_LARGE_M;
+            const int64_t bm = gemm_bm(p.variant);
+            const int64_t nt2 = (d + gemm2_bn(p.variant) - 1) / gemm2_bn(p.variant);
+            int64_t mt = (R + bm - 1) / bm;
+            if (mt < busy_experts) mt = busy_experts;
+            const int64_t tiles = nt2 * mt;
+            // Cut the w2 contraction when GEMM 2 alone would not give every CU
+            // a couple of workgroups; keep at least 4 K steps per slice.
+            int64_t s = (512 + tiles - 1) / tiles;
+            const int64_t kt = f / 64;
+            int64_t smax = kt / 4 < 8 ? kt / 4 : 8;
+            if (smax < 1) smax = 1;
+            if (s > smax) s = smax;
+            if (s < 1) s = 1;
+            p.splits = (int)s;
+        }
     }
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -229,7 +256,15 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     mark(2);
     LAUNCH(launch_gather_rows(dtype, x, row_token, R, di, x_perm, stream), "gather_rows");
     mark(3);
-    if (dtype == MOE_DTYPE_BF16) {
+    if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM) {
+        LAUNCH(launch_gemm1_swiglu_stream(x_perm, w1, w3, offsets, R, Ei, di, fi, h, stream), "gemm1_swiglu");
+        mark(4);
+        LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");
+    } else if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_TILE256) {
+        LAUNCH(launch_gemm1_swiglu_tile(x_perm, w1, w3, offsets, R, Ei, di, fi, h, stream), "gemm1_swiglu");
+        mark(4);
+        LAUNCH(launch_gemm2_tile(h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");
+    } else if (dtype == MOE_DTYPE_BF16) {
         LAUNCH(launch_gemm1_swiglu_bf16(plan.variant, x_perm, w1, w3, offsets, R, Ei, di, fi, h, stream), "gemm1_swiglu");
         mark(4);
         LAUNCH(launch_gemm2_bf16(plan.variant, h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");

@@ -59,6 +59,22 @@ hipError_t launch_gemm2_bf16(int variant, const void* h, const void* w2, const i
 hipError_t launch_gemm2_f32(const void* h, const void* w2, const int32_t* offsets, int R, int E,
                             int f, int d, float* y, hipStream_t stream);
 
+// The same two contractions for batches with few rows per expert: weights are
+// streamed from HBM into registers (16-row tiles, 128-column slabs).
+hipError_t launch_gemm1_swiglu_stream(const void* x_perm, const void* w1, const void* w3,
+                                      const int32_t* offsets, int R, int E, int d, int f, void* h,
+                                      hipStream_t stream);
+hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* offsets, int R, int E,
+                               int f, int d, int splits, float* y, hipStream_t stream);
+
+// The same two contractions for batches with many rows per expert: 256x256
+// macro tiles, double-buffered LDS.
+hipError_t launch_gemm1_swiglu_tile(const void* x_perm, const void* w1, const void* w3,
+                                    const int32_t* offsets, int R, int E, int d, int f, void* h,
+                                    hipStream_t stream);
+hipError_t launch_gemm2_tile(const void* h, const void* w2, const int32_t* offsets, int R, int E,
+                             int f, int d, int splits, float* y, hipStream_t stream);
+
 // out[t,:] = (residual[t,:] +) sum_j gates[t,j] * sum_s y[s][slot_row[t*k+j], :]
 hipError_t launch_combine(int dtype, const float* y, int splits, const float* gates,
                           const int32_t* slot_row, const void* residual, int T, int d, int k, int R,
@@ -72,7 +88,7 @@ hipError_t launch_rmsnorm(int dtype, const void* h, void* x, int T, int d, float
                           hipStream_t stream);
 
 // Tile shapes of the bf16 grouped GEMMs, chosen by the host per call.
-enum GemmVariant { GEMM_LARGE_M = 0, GEMM_SMALL_M = 1 };
+enum GemmVariant { GEMM_LARGE_M = 0, GEMM_SMALL_M = 1, GEMM_STREAM = 2, GEMM_TILE256 = 3 };
 int gemm_bm(int variant);      // rows per tile
 int gemm1_bn(int variant);     // h columns per tile
 int gemm2_bn(int variant);     // y columns per tile

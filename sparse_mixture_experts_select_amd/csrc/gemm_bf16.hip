@@ -157,15 +157,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
     // A: chunks tid + 256*i of the BM x 64 tile (8 chunks of 16 B per row).
     const bf16* a_src[G::A_CHUNKS];
     int a_lds[G::A_CHUNKS];
-    bool a_ok[G::A_CHUNKS];
 #pragma unroll
     for (int i = 0; i < G::A_CHUNKS; ++i) {
         const int chunk = tid + kThreads * i;
         const int row = chunk >> 3;
         const int c = chunk & 7;
-        const int grow = ti.row0 + row;
-        a_ok[i] = grow < ti.row_end;
-        a_src[i] = A + (size_t)(a_ok[i] ? grow : ti.row0) * K + c * 8;
+        const int grow = min(ti.row0 + row, ti.row_end - 1);
+        a_src[i] = A + (size_t)grow * K + c * 8;
         a_lds[i] = row * kBK + a_slot(row, c) * 8;
     }
     // B: one 8x8 (k x n) block per thread.
@@ -191,17 +189,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(
     uint4 rb[8];
 
     auto load_global = [&](int kt) {
+        // Unconditional loads: out-of-range rows and columns read clamped,
+        // valid addresses and only feed outputs that are never stored.
 #pragma unroll
-        for (int i = 0; i < G::A_CHUNKS; ++i) {
-            if (a_ok[i]) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + (size_t)kt * kBK);
-            else ra[i] = make_uint4(0, 0, 0, 0);
-        }
+        for (int i = 0; i < G::A_CHUNKS; ++i)
+            ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + (size_t)kt * kBK);
         const bf16* p = b_src + (size_t)kt * kBK * N;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if (b_ok) rb[r] = *reinterpret_cast<const uint4*>(p + (size_t)r * N);
-            else rb[r] = make_uint4(0, 0, 0, 0);
-        }
+        for (int r = 0; r < 8; ++r) rb[r] = *reinterpret_cast<const uint4*>(p + (size_t)r * N);
     };
     auto store_lds = [&]() {
 #pragma unroll

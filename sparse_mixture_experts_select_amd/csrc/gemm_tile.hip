@@ -1,0 +1,354 @@
+// gemm_tile.hip -- the expert contractions for batches with many rows per
+// expert (prefill), where the time is MFMA work: 256x256 macro tiles.
+//
+// Same products as the other GEMM files (Mixtral of Experts, wikillm.com card,
+// "Method", SwiGLU pseudocode): per expert e over its grouped rows,
+//   GEMM 1:  h = SiLU(X_e . w1[e]) * (X_e . w3[e])
+//   GEMM 2:  y = h_e . w2[e]   (fp32, optionally in K slices)
+//
+// Workgroup: 256 threads = 4 wavefronts in a 2x2 grid.  Macro tile: 256 rows x
+// 256 weight columns (GEMM 1: 128 columns of w1 and the same 128 of w3; GEMM 2:
+// 256 columns of w2), K step 32.  Each wave owns a 128 x 128 block of
+// accumulators (8 x 8 fragments of v_mfma_f32_16x16x32_bf16, 256 fp32 per
+// lane, held in AGPRs), so every fragment read from LDS feeds 8 MFMAs.
+//
+// Staging: global -> LDS by DMA (buffer_load_dwordx4 ... lds: lane l's 16
+// bytes land at the wave's LDS base + 16 l).  SGPR buffer descriptors over A
+// and the expert's weights; each lane's byte offset is fixed for the whole
+// loop and a wave-uniform offset advances per K step.  Four LDS stages of
+// 32 KiB; loads run three K steps ahead, always exactly three (past the end
+// the refills repeat the last step: valid addresses, never read), so one
+// fixed wait, vmcnt(16), leaves each step's own loads complete.  No register
+// holds staged data and no VALU work is spent on it.  After that wait, one
+// barrier per step publishes the stage to all waves and frees the stage read
+// in the previous step; it is a raw s_barrier after lgkmcnt(0), between
+// compiler-only fences, so loads of later steps stay in flight across it.
+// Each stage is its own LDS array and the K loop is unrolled by four, so every
+// read and every refill names a fixed array; where the compiler can see that a
+// read does not depend on the refills in flight it adds no wait of its own.
+//
+// LDS layouts (both bank-conflict free for the fragment reads):
+//   A stage: [256 rows][32 k], 64 bytes per row; the row's four 16-byte
+//     chunks are stored XOR (row/4)%4, so 16 rows x one chunk cover 256 bytes.
+//   B stage: two halves of [32 k][128 n] (GEMM 1: w1 | w3; GEMM 2: columns
+//     0..127 | 128..255), the weights' own orientation (n contiguous), 256
+//     bytes per k row in 32-byte groups of 16 columns; group G of row k is
+//     stored at G XOR ((k%4) | ((k/8)%2) << 2).  A B fragment (8 k x 16 n per
+//     lane group) is read with two ds_read_b64_tr_b16, which hand each lane 4
+//     consecutive k of one column from a 4 x 16 tile whose rows the 16 lanes
+//     address in 8-byte pieces.
+// The DMA lane order fixes the LDS address, so each lane simply loads the
+// global chunk that belongs at its swizzled LDS position.
+//
+// Order.  Tiles are numbered (expert, K slice, n-tile, m-tile), m fastest, and
+// each XCD takes a contiguous run of them (workgroup IDs are dealt to the 8
+// XCDs round-robin), so workgroups that share a weight panel run together and
+// share one L2.
+//
+// Epilogue.  GEMM 1 forms SiLU(a) * b, stages the bf16 tile in LDS (two of the
+// stage arrays, 16-byte chunks XOR-swizzled by row) and writes it with 16-byte
+// row-contiguous stores.  GEMM 2 writes fp32 straight from the
+// accumulators (64-byte row segments per fragment).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 256;
+constexpr int kBK = 32;
+constexpr int kCols = 256;                             // weight columns staged per step
+constexpr int kStages = 4;
+constexpr int kAUnits = kBM * kBK / 8;                 // 1024 16-byte units
+constexpr int kBUnits = kBK * kCols / 8;               // 1024 16-byte units
+constexpr int kStageBytes = (kAUnits + kBUnits) * 16;  // 32 KiB
+constexpr int kBOffset = kAUnits * 16;                 // B part of a stage
+constexpr int kBHalfBytes = kBK * 128 * 2;             // one 128-column half of B
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+
+__device__ __forceinline__ int b_group_swz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
+#define MOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | (((n) >> 4) << 14))
+
+// Barrier between K steps: this wave's LDS reads are complete (lgkmcnt(0)),
+// so the stage it read last can be refilled once every wave has arrived; the
+// compiler-only fences keep memory accesses from moving across it, and DMA
+// loads of later steps stay in flight.
+__device__ __forceinline__ void stage_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <bool DUAL>
+__global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
+    const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
+    void* __restrict__ C, const int32_t* __restrict__ offsets, int R, int E, int K, int N,
+    int splits) {
+    constexpr int BN = DUAL ? 128 : 256;  // output columns per tile
+    // One array per stage: the compiler can then tell the stage being read
+    // from the stages the DMA is writing, and does not wait for those loads.
+    __shared__ __align__(16) unsigned char st0[kStageBytes];
+    __shared__ __align__(16) unsigned char st1[kStageBytes];
+    __shared__ __align__(16) unsigned char st2[kStageBytes];
+    __shared__ __align__(16) unsigned char st3[kStageBytes];
+
+    // ---- tile lookup
+    const int NT = (N + BN - 1) / BN;
+    int total = 0;
+    for (int e = 0; e < E; ++e) {
+        const int n_e = offsets[e + 1] - offsets[e];
+        total += ((n_e + kBM - 1) / kBM) * NT * splits;
+    }
+    const int per_xcd = (total + 7) / 8;
+    const int slot = blockIdx.x >> 3;
+    if (slot >= per_xcd) return;
+    int L = (blockIdx.x & 7) * per_xcd + slot;
+    if (L >= total) return;
+    int e = 0, row0 = 0, row_end = 0, n_tile = 0, split = 0;
+    for (e = 0; e < E; ++e) {
+        const int o0 = offsets[e];
+        const int n_e = offsets[e + 1] - o0;
+        const int mt = (n_e + kBM - 1) / kBM;
+        const int tiles = mt * NT * splits;
+        if (L < tiles) {
+            const int m = L % mt;
+            const int rest = L / mt;
+            n_tile = rest % NT;
+            split = rest / NT;
+            row0 = o0 + m * kBM;
+            row_end = o0 + n_e;
+            break;
+        }
+        L -= tiles;
+    }
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int col0 = n_tile * BN;
+
+    const int KT = K / kBK;
+    const int kt_per = (KT + splits - 1) / splits;
+    const int kt0 = min(split * kt_per, KT);
+    const int kt1 = min(kt0 + kt_per, KT);
+
+    // ---- DMA sources.  Buffer descriptors (SGPRs) over A and over the
+    // expert's weight matrices; per lane a loop-invariant byte offset, per K
+    // step a wave-uniform one.  Unit u = 256 i + 64 wave + lane (i = 0..3) of
+    // each stage part; the wave's LDS destination for instruction i is
+    // part base + (256 i + 64 wave) * 16.
+    const __amdgpu_buffer_rsrc_t a_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0x7fffffff, 0x00020000);
+    const bf16* bh0 = B0 + (size_t)e * K * N;
+    const bf16* bh1 = (DUAL ? B1 : B0) + (size_t)e * K * N;
+    const __amdgpu_buffer_rsrc_t b_rsrc0 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)bh0, (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t b_rsrc1 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)bh1, (short)0, 0x7fffffff, 0x00020000);
+    int a_voff[4];
+    int b_voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int u = 256 * i + 64 * wave + lane;
+        // A: row r = u/4; stored chunk u%4 holds logical chunk (u%4) ^ ((r/4)%4).
+        const int r = u >> 2;
+        const int c = (u & 3) ^ ((r >> 2) & 3);
+        const int grow = min(row0 + r, row_end - 1);  // rows past the expert only feed unstored rows
+        a_voff[i] = (grow * K + 8 * c) * 2;
+        // B: half h = u/512 (instructions 0,1 -> half 0, 2,3 -> half 1); within
+        // the half, k row kk = (u%512)/16 and stored unit p = u%16 is group
+        // (p/2) ^ swz(kk), 8-column piece p%2.
+        const int v = u & 511;
+        const int kk = v >> 4;
+        const int p = v & 15;
+        const int col = 16 * ((p >> 1) ^ b_group_swz(kk)) + 8 * (p & 1);
+        int gcol = (DUAL ? col0 : col0 + 128 * (i >> 1)) + col;
+        if (gcol >= N) gcol = 0;  // columns past N only feed unstored columns
+        b_voff[i] = (kk * N + gcol) * 2;
+    }
+    const int a_step = kBK * 2;      // bytes per K step in A
+    const int b_step = kBK * N * 2;  // bytes per K step in B
+
+    // ---- fragment addressing (bytes within a stage)
+    const int lrow = lane & 15;
+    const int lgrp = lane >> 4;
+    // A fragment m: row wm*128 + 16 m + lrow, chunk lgrp, stored at chunk
+    // lgrp ^ ((row/4)%4) = lgrp ^ ((lrow/4)%4) for every m.
+    const int a_frag = (wm * 128 + lrow) * 64 + 16 * (lgrp ^ ((lrow >> 2) & 3));
+    // B fragment n: 16 columns of one half; lane (lgrp, lrow) addresses k row
+    // 8 lgrp + lrow/4 (+4 for the second read), columns 4 (lrow%4) .. +3.
+    const int b_k = 8 * lgrp + (lrow >> 2);
+    const int b_swz = b_group_swz(b_k);  // the same for b_k + 4
+    int b_frag[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        int half, g;
+        if (DUAL) {
+            half = n >> 2;
+            g = 4 * wn + (n & 3);
+        } else {
+            half = wn;
+            g = n;
+        }
+        b_frag[n] = kBOffset + half * kBHalfBytes + b_k * 256 + 32 * (g ^ b_swz) + 8 * (lrow & 3);
+    }
+
+    floatx4 acc[8][8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+#define MOE_ISSUE_STAGE(KT_, ARR_)                                                          \
+    do {                                                                                    \
+        lds_char* sb_ = (lds_char*)(lds_void*)(ARR_) + (64 * wave) * 16;                    \
+        const int ka_ = (KT_) * a_step;                                                     \
+        const int kb_ = (KT_) * b_step;                                                     \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                    \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void*)(sb_ + 4096 * i_), \
+                                                     16, a_voff[i_], ka_, 0, 0);            \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                    \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(i_ < 2 ? b_rsrc0 : b_rsrc1,           \
+                                                     (lds_void*)(sb_ + kBOffset + 4096 * i_), \
+                                                     16, b_voff[i_], kb_, 0, 0);            \
+    } while (0)
+
+    // One K step on stage array CUR_: refill NEXT_ (the stage read in the
+    // previous step) with step kt + 3, then read CUR_'s fragments and run the
+    // MFMAs, one B fragment at a time.
+#define MOE_STEP(CUR_, NEXT_)                                                               \
+    if (kt < kt1) {                                                                         \
+        MOE_WAIT_VM(16);                                                                    \
+        stage_barrier();                                                                    \
+        MOE_ISSUE_STAGE(min(kt + 3, kt1 - 1), NEXT_);                                       \
+        const lds_char* st_ = (const lds_char*)(lds_void*)(CUR_);                           \
+        bf16x8 af_[8];                                                                      \
+        _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_)                                    \
+            af_[m_] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(   \
+                st_ + a_frag + m_ * 16 * 64);                                               \
+        _Pragma("unroll") for (int n_ = 0; n_ < 8; ++n_) {                                  \
+            const short4_t lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                   \
+                (lds_short4*)(st_ + b_frag[n_]));                                           \
+            const short4_t hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                   \
+                (lds_short4*)(st_ + b_frag[n_] + 4 * 256));                                 \
+            const bf16x8 bf_ = __builtin_bit_cast(                                          \
+                bf16x8, __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7));         \
+            _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_)                                \
+                acc[m_][n_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af_[m_], bf_,         \
+                                                                      acc[m_][n_], 0, 0, 0); \
+        }                                                                                   \
+        ++kt;                                                                               \
+    }
+
+    // Loads in flight: the prologue fills st0, st1, st2 with steps kt0,
+    // kt0+1, kt0+2; each step refills one stage, so exactly three younger
+    // steps are in flight at every step's wait and one fixed vmcnt(16) leaves
+    // the step's own loads complete.  Past the last step the refills repeat it
+    // (valid addresses, never read).
+    int kt = kt0;
+    if (kt0 < kt1) {
+        MOE_ISSUE_STAGE(kt0, st0);
+        MOE_ISSUE_STAGE(min(kt0 + 1, kt1 - 1), st1);
+        MOE_ISSUE_STAGE(min(kt0 + 2, kt1 - 1), st2);
+        while (kt < kt1) {
+            MOE_STEP(st0, st3)
+            MOE_STEP(st1, st0)
+            MOE_STEP(st2, st1)
+            MOE_STEP(st3, st2)
+        }
+    }
+#undef MOE_STEP
+#undef MOE_ISSUE_STAGE
+    // No load may still be writing LDS when the stages are reused below.
+    MOE_WAIT_VM(0);
+
+    // ---- epilogue: lane holds rows 4*lgrp + r (r = 0..3) of column lrow of each fragment.
+    if (DUAL) {
+        __syncthreads();  // every wave is done reading the stages
+        // Stage the 256 x 128 bf16 tile of h in LDS: rows 0..127 (wm = 0) in
+        // st0, rows 128..255 in st1, 256 bytes per row, 16-byte chunk ch of
+        // row r stored at ch ^ (r % 16).
+        uint16_t* hs_w = reinterpret_cast<uint16_t*>(wm == 0 ? st0 : st1);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * m + 4 * lgrp + r;  // within this wave's 128 rows
+                    const int c = wn * 64 + 16 * n + lrow;
+                    const float hv = silu_f32(acc[m][n][r]) * acc[m][n + 4][r];
+                    hs_w[row * 128 + (((c >> 3) ^ (row & 15)) << 3) + (c & 7)] =
+                        (uint16_t)f32_to_bf16_bits(hv);
+                }
+        __syncthreads();
+        uint16_t* h = reinterpret_cast<uint16_t*>(C);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int idx = tid + kThreads * q;
+            const int row = idx >> 4;   // 0..255
+            const int ch = idx & 15;    // 16-byte chunk of the row
+            const int grow = row0 + row;
+            const int gc = col0 + ch * 8;
+            const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(row < 128 ? st0 : st1);
+            const int rr = row & 127;
+            if (grow < row_end && gc < N)
+                *reinterpret_cast<uint4*>(h + (size_t)grow * N + gc) =
+                    *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
+        }
+    } else {
+        float* y = reinterpret_cast<float*>(C) + (size_t)split * R * N;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int grow = row0 + wm * 128 + 16 * m + 4 * lgrp + r;
+                if (grow >= row_end) continue;
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    const int gc = col0 + wn * 128 + 16 * n + lrow;
+                    if (gc < N) y[(size_t)grow * N + gc] = acc[m][n][r];
+                }
+            }
+    }
+}
+
+template <bool DUAL>
+hipError_t launch_tile(const void* A, const void* B0, const void* B1, void* C,
+                       const int32_t* offsets, int R, int E, int K, int N, int splits,
+                       hipStream_t stream) {
+    const long long BN = DUAL ? 128 : 256;
+    const long long NT = (N + BN - 1) / BN;
+    const long long mtiles = (R + kBM - 1) / kBM + E;  // bound on sum_e ceil(n_e / 256)
+    long long grid = mtiles * NT * splits;
+    grid = (grid + 7) / 8 * 8;
+    hipLaunchKernelGGL((tile_gemm_kernel<DUAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const bf16*>(A), reinterpret_cast<const bf16*>(B0),
+                       reinterpret_cast<const bf16*>(B1), C, offsets, R, E, K, N, splits);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm1_swiglu_tile(const void* x_perm, const void* w1, const void* w3,
+                                    const int32_t* offsets, int R, int E, int d, int f, void* h,
+                                    hipStream_t stream) {
+    return launch_tile<true>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
+}
+
+hipError_t launch_gemm2_tile(const void* h, const void* w2, const int32_t* offsets, int R, int E,
+                             int f, int d, int splits, float* y, hipStream_t stream) {
+    return launch_tile<false>(h, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+}
+
+}  // namespace moe

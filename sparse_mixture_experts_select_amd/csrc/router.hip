@@ -8,10 +8,12 @@
 //
 // One wavefront handles TPW tokens at a time.  The router matrix [d,E] is
 // staged once per workgroup in LDS when it fits (64 KiB for d=4096, E=8 in
-// bf16) and read from there for every token of the workgroup.  Each lane
-// accumulates fp32 partial logits over a strided slice of d (16-byte loads of
-// x), a butterfly of cross-lane adds gives every lane the full logits, and
-// the selection runs redundantly on all lanes; lane 0 stores it.
+// bf16), transposed to [E][d] so that a lane reads the 16 contiguous bytes of
+// one expert's column that match its 16-byte slice of x (consecutive lanes,
+// consecutive addresses: no bank conflicts).  Each lane accumulates fp32
+// partial logits over a strided set of 16-byte slices of d, a butterfly of
+// cross-lane adds gives every lane the full logits, and the selection runs
+// redundantly on all lanes; lane 0 stores it.
 //
 // Logits stay fp32 (products of bf16 inputs are exact in fp32, sums are
 // fp32).  Ties break toward the lower expert index; the picks are stored by
@@ -56,23 +58,41 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias, int T_,
     int d, int E, int k, int use_lds, int32_t* __restrict__ ids, float* __restrict__ gates) {
     extern __shared__ __align__(16) unsigned char lds_raw[];
-    T* wl = reinterpret_cast<T*>(lds_raw);
+    T* wt = reinterpret_cast<T*>(lds_raw);  // [E][d] when use_lds
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    constexpr int VN = Vec<T>::N;
 
-    const T* wsrc = wr;
     if (use_lds) {
-        // Copy the router matrix into LDS with 16-byte moves (d*E*sizeof(T)
-        // is a multiple of 16 because d is a multiple of the vector width).
-        const int nvec = d * E * (int)sizeof(T) / 16;
-        const uint4* s = reinterpret_cast<const uint4*>(wr);
-        uint4* dst = reinterpret_cast<uint4*>(wl);
-        for (int i = threadIdx.x; i < nvec; i += kThreads) dst[i] = s[i];
+        // Transposing copy: flat element q of w_router is (i, e) = (q / E, q % E);
+        // (i, e) advance incrementally, so the loop has no division.
+        const int n = d * E;
+        const int step = kThreads * VN;
+        const int di = step / E, de = step - (step / E) * E;
+        int q0 = threadIdx.x * VN;
+        int i0 = q0 / E, e0 = q0 - i0 * E;
+        for (; q0 < n; q0 += step) {
+            float v[VN];
+            Vec<T>::load(wr + q0, v);
+            int i = i0, e = e0;
+#pragma unroll
+            for (int u = 0; u < VN; ++u) {
+                wt[(size_t)e * d + i] = (T)v[u];
+                if (++e == E) {
+                    e = 0;
+                    ++i;
+                }
+            }
+            i0 += di;
+            e0 += de;
+            if (e0 >= E) {
+                e0 -= E;
+                ++i0;
+            }
+        }
         __syncthreads();
-        wsrc = wl;
     }
 
-    constexpr int VN = Vec<T>::N;
     const int stride = 64 * VN;
     const int groups = (T_ + TPW - 1) / TPW;
     for (int grp = blockIdx.x * kWaves + wave; grp < groups; grp += gridDim.x * kWaves) {
@@ -95,15 +115,19 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
                 }
             }
 #pragma unroll
-            for (int u = 0; u < VN; ++u) {
-                const T* wrow = wsrc + (size_t)(i0 + u) * E;
+            for (int e = 0; e < EMAX; ++e) {
+                if (e < E) {
+                    float w[VN];
+                    if (use_lds) {
+                        Vec<T>::load(wt + (size_t)e * d + i0, w);
+                    } else {
 #pragma unroll
-                for (int e = 0; e < EMAX; ++e) {
-                    if (e < E) {
-                        const float w = Vec<T>::one(wrow, e);
-#pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt) acc[tt][e] = fmaf(xv[tt][u], w, acc[tt][e]);
+                        for (int u = 0; u < VN; ++u) w[u] = Vec<T>::one(wr, (i0 + u) * E + e);
                     }
+#pragma unroll
+                    for (int u = 0; u < VN; ++u)
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt) acc[tt][e] = fmaf(xv[tt][u], w[u], acc[tt][e]);
                 }
             }
         }
@@ -186,6 +210,8 @@ hipError_t launch_t(const void* x, const void* wr, const float* bias, int T_, in
 template <typename T>
 hipError_t dispatch_e(const void* x, const void* wr, const float* bias, int T_, int d, int E,
                       int k, int32_t* ids, float* gates, hipStream_t stream) {
+    // Small batches: one token per wave, to spread them over more CUs.
+    if (E <= 8 && T_ <= 2048) return launch_t<T, 8, 1>(x, wr, bias, T_, d, E, k, ids, gates, stream);
     if (E <= 8) return launch_t<T, 8, 4>(x, wr, bias, T_, d, E, k, ids, gates, stream);
     if (E <= 16) return launch_t<T, 16, 2>(x, wr, bias, T_, d, E, k, ids, gates, stream);
     if (E <= 32) return launch_t<T, 32, 1>(x, wr, bias, T_, d, E, k, ids, gates, stream);

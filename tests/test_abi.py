@@ -121,6 +121,7 @@ def test_workspace_bytes(binding):
     R = T * k
     n = binding.moe_ffn_workspace_bytes(T, d, f, E, k, binding.MOE_DTYPE_BF16)
     floor = R * d * 2 + R * f * 2 + R * d * 4
-    assert floor <= n <= floor + 64 * 1024 * 1024
+    # at most two fp32 K-slice partials of y, plus small index arrays
+    assert floor <= n <= floor + R * d * 4 + 64 * 1024 * 1024
     assert binding.moe_ffn_workspace_bytes(4, 96, 128, 8, 2, binding.MOE_DTYPE_BF16) == 0
     assert binding.moe_ffn_workspace_bytes(64, 128, 256, 8, 2, binding.MOE_DTYPE_F32) > 0

@@ -47,6 +47,14 @@ SMALL = [
     (33, 64, 128, 1, 1, torch.bfloat16),      # E = 1: plain SwiGLU
     (100, 128, 128, 64, 8, torch.bfloat16),   # widest routing
     (700, 256, 256, 8, 2, torch.bfloat16),    # several 128-row tiles per expert
+    # 256x256 macro tiles (at least 128 rows per expert on average)
+    (1100, 256, 384, 8, 2, torch.bfloat16),   # partial last row tiles, K split 2 in GEMM 2
+    (600, 192, 320, 4, 2, torch.bfloat16),    # ragged columns in both GEMMs
+    (2000, 128, 256, 8, 1, torch.bfloat16),   # k = 1, 250 rows per expert
+    # streamed-weight path (about a dozen rows or fewer per expert)
+    (48, 192, 320, 8, 2, torch.bfloat16),     # ragged slabs, experts above 16 rows, K split 2
+    (20, 256, 1024, 8, 2, torch.bfloat16),    # K split 8, one step per wave
+    (5, 128, 128, 64, 8, torch.bfloat16),     # E = 64, most experts empty
     (50, 100, 60, 5, 2, torch.float32),
     (200, 64, 96, 16, 4, torch.float32),
 ]
@@ -81,6 +89,14 @@ def test_imbalanced_and_empty_experts():
     r = PT.full_check(inp, 2)
     counts = PT.to_np(r["gpu"]["counts"])
     assert counts[3] == 300 and counts[5:].sum() == 0
+
+
+def test_streamed_path_with_one_heavy_expert():
+    banner("streamed path, expert 2 takes all 40 tokens (3 row tiles)")
+    bias = [0.0, 0.0, 40.0, 0.0, 0.0, 0.0, 0.0, 0.0]
+    inp = case(40, 128, 256, 8, torch.bfloat16, seed=11, bias=bias, label="heavy")
+    r = PT.full_check(inp, 2)
+    assert PT.to_np(r["gpu"]["counts"])[2] == 40
 
 
 def test_zero_tokens_leaves_out_untouched():
