@@ -32,7 +32,20 @@ if ROOT not in sys.path:
 METRIC = "MoE FFN tokens/s at Mixtral shapes; % MFMA peak (prefill), % HBM BW (decode)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-GEMM1_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_select_amd", "csrc", "gemm_bf16.hip")
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_select_amd", "csrc")
+# The w1/w3 grouped GEMM that runs for each workload: the streamed-weight
+# kernel at a few rows per expert, the 256x256 tile kernel at >= 128 rows per
+# expert.  Patterns match both the demangled and the mangled kernel name.
+GEMM1_KERNEL = {
+    "decode": ("gemm_stream.hip", r"stream_gemm_kernel(<true, false>|ILb1ELb0E)"),
+    "prefill": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
+    "skewed": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
+}
+CALIBRATION_BYTES = 1 << 30
+PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d gpurun_out/pmc_{tag} -o run -- "
+               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy")
+TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o run -- "
+                 "python3 bench.py --steps 10 --warmup 2 --cpu-seconds 2")
 
 
 def log(*a):
@@ -58,9 +71,14 @@ def layer_algorithmic(wl, counts):
     return flops, nbytes
 
 
-def source_digest(path):
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def source_digest(workload):
+    """Digest of the source of the w1/w3 kernel the workload runs (plus the
+    shared header), to tell whether committed counter figures still apply."""
+    h = hashlib.sha256()
+    for name in (GEMM1_KERNEL[workload][0], "common.h"):
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def committed_traffic(workload):
@@ -75,7 +93,7 @@ def committed_traffic(workload):
             if "=" in line and not line.lstrip().startswith("#"):
                 key, val = line.split("=", 1)
                 vals[key.strip()] = val.strip()
-    if vals.get("kernel_source_sha256_16") != source_digest(GEMM1_SOURCE):
+    if vals.get("kernel_source_sha256_16") != source_digest(workload):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -180,7 +198,7 @@ def cpu_baseline(res, seconds, inputs):
                       % (wl.name, n_tok - 1, reps, el)}
 
 
-def calibrate_copy(torch, nbytes=1 << 30, reps=3):
+def calibrate_copy(torch, nbytes=CALIBRATION_BYTES, reps=3):
     """Plain device-to-device copies of a known size (reference for the
     FETCH_SIZE / WRITE_SIZE counters)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
@@ -189,6 +207,133 @@ def calibrate_copy(torch, nbytes=1 << 30, reps=3):
         dst.copy_(src)
     torch.cuda.synchronize()
     log("[bench] calibration copy: %d x %d bytes" % (reps, nbytes))
+
+
+def _counter_rows(run_dir):
+    import csv
+    path = os.path.join(run_dir, "run_counter_collection.csv")
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """Turn two rocprofv3 --pmc runs of PMC_COMMAND (FETCH_SIZE, then
+    WRITE_SIZE) into profiles/gemm1_swiglu_<workload>_traffic.txt: HBM bytes
+    per launch of the w1/w3 kernel, each counter scaled by what it reads for
+    the 1 GiB calibration copies run in the same process."""
+    import re
+    import statistics
+
+    rows = {"FETCH_SIZE": _counter_rows(fetch_dir), "WRITE_SIZE": _counter_rows(write_dir)}
+    factor, calib = {}, {}
+    for name, rs in rows.items():
+        vals = [float(r["Counter_Value"]) for r in rs
+                if r["Counter_Name"] == name and "copyBuffer" in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit("no calibration copy dispatches in the %s run" % name)
+        calib[name] = statistics.median(vals)
+        factor[name] = CALIBRATION_BYTES / (calib[name] * 1024.0)
+    written = []
+    for wl, (src, pattern) in GEMM1_KERNEL.items():
+        per = {}
+        for name, rs in rows.items():
+            vals = [float(r["Counter_Value"]) for r in rs
+                    if r["Counter_Name"] == name and re.search(pattern, r["Kernel_Name"])]
+            if vals:
+                per[name] = vals
+        if len(per) != 2 or wl == "skewed":
+            continue
+        fetch_kib = statistics.mean(per["FETCH_SIZE"])
+        write_kib = statistics.mean(per["WRITE_SIZE"])
+        hbm = fetch_kib * 1024.0 * factor["FETCH_SIZE"] + write_kib * 1024.0 * factor["WRITE_SIZE"]
+        out = os.path.join(ROOT, "profiles", "gemm1_swiglu_%s_traffic.txt" % wl)
+        with open(out, "w") as fh:
+            fh.write("# HBM traffic of the w1/w3 grouped GEMM + SwiGLU kernel, %s workload\n" % wl)
+            fh.write("# kernel: %s (source %s)\n" % (pattern, src))
+            for name in ("FETCH_SIZE", "WRITE_SIZE"):
+                fh.write("# command (%s): %s\n" % (name, PMC_COMMAND.format(
+                    counter=name, tag=name.split("_")[0].lower())))
+            fh.write("# summarized by: python3 bench.py --summarize-counters gpurun_out/pmc_fetch "
+                     "gpurun_out/pmc_write\n")
+            fh.write("# calibration: %d-byte device copy reads FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f "
+                     "KiB\n" % (CALIBRATION_BYTES, calib["FETCH_SIZE"], calib["WRITE_SIZE"]))
+            fh.write("fetch_scale = %.4f\n" % factor["FETCH_SIZE"])
+            fh.write("write_scale = %.4f\n" % factor["WRITE_SIZE"])
+            fh.write("launches = %d\n" % len(per["FETCH_SIZE"]))
+            fh.write("fetch_kib_per_launch = %.1f\n" % fetch_kib)
+            fh.write("write_kib_per_launch = %.1f\n" % write_kib)
+            fh.write("hbm_bytes_per_launch = %.0f\n" % hbm)
+            fh.write("kernel_source_sha256_16 = %s\n" % source_digest(wl))
+        written.append(out)
+    for out in written:
+        log("[bench] wrote", out)
+    if not written:
+        raise SystemExit("no w1/w3 kernel dispatches found")
+
+
+def _short_kernel_name(name):
+    """Readable kernel name: the library's mangled names (plain function
+    templates over bool / int / bf16 / float) are decoded by hand."""
+    import re
+    m = re.match(r"_ZN3moe12_GLOBAL__N_1(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        base = name[m.end():m.end() + n]
+        rest = name[m.end() + n:]
+        if rest.startswith("I"):
+            args = []
+            for tok in re.finditer(r"Lb([01])E|Li(-?\d+)E|DF16b|f", rest[1:rest.index("EE") + 1]):
+                if tok.group(1) is not None:
+                    args.append("true" if tok.group(1) == "1" else "false")
+                elif tok.group(2) is not None:
+                    args.append(tok.group(2))
+                else:
+                    args.append("bf16" if tok.group(0) == "DF16b" else "float")
+            base += "<%s>" % ", ".join(args)
+        return base
+    name = name.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+    depth = 0
+    for i, ch in enumerate(name):
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def summarize_trace(trace_dir):
+    """Condense the --kernel-trace output of TRACE_COMMAND into
+    profiles/moe_layer_decode_prefill_kernel_stats.txt: per kernel and grid
+    size (which tells the decode launches from the prefill ones) the number of
+    calls and the average / min / max duration."""
+    import csv
+    import statistics
+    with open(os.path.join(trace_dir, "run_kernel_trace.csv")) as fh:
+        rows = list(csv.DictReader(fh))
+    groups = {}
+    for r in rows:
+        if "moe" not in r["Kernel_Name"] and "copyBuffer" not in r["Kernel_Name"]:
+            continue
+        key = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        g = groups.setdefault(key, {"d": [], "first": int(r["Dispatch_Id"]), "row": r})
+        g["d"].append(dur)
+    out = os.path.join(ROOT, "profiles", "moe_layer_decode_prefill_kernel_stats.txt")
+    with open(out, "w") as fh:
+        fh.write("# rocprofv3 kernel trace of the benchmark: decode (T=32), then prefill "
+                 "(T=4096); d=4096 f=14336 E=8 k=2 bf16\n")
+        fh.write("# command: %s\n" % TRACE_COMMAND)
+        fh.write("# summarized by: python3 bench.py --summarize-trace gpurun_out/trace\n")
+        fh.write("# calls = warm-up + one routing probe call + timed steps; durations in us; "
+                 "grid in work-items; torch's input generation kernels left out\n")
+        fh.write("%-44s %9s %6s %10s %10s %10s %5s %5s %6s\n" % (
+            "kernel", "grid", "calls", "avg_us", "min_us", "max_us", "vgpr", "agpr", "lds"))
+        for (name, grid), g in sorted(groups.items(), key=lambda kv: kv[1]["first"]):
+            r = g["row"]
+            fh.write("%-44s %9d %6d %10.2f %10.2f %10.2f %5s %5s %6s\n" % (
+                name[:44], grid, len(g["d"]), statistics.mean(g["d"]), min(g["d"]), max(g["d"]),
+                r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"]))
+    log("[bench] wrote", out)
 
 
 def main():
@@ -201,7 +346,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this layer is benchmarked on a single MI355X "
