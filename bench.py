@@ -8,10 +8,12 @@ which is HBM-bound; the T=4096 prefill batch (MFMA-bound) is reported beside
 it under "secondary".
 
 Live timing: the K timed steps are bracketed by torch.cuda.synchronize();
-inside them the library records HIP events at every stage boundary on the
-launch stream (moe_ffn_profile_begin/end), which gives the average duration
-of each kernel over the timed region.  The roofline entry is for the dominant
-kernel (the w1/w3 grouped GEMM with the SwiGLU epilogue).
+inside them the library records HIP events on the launch stream just before
+and just after the dominant kernel (the w1/w3 grouped GEMM with the SwiGLU
+epilogue; moe_ffn_profile_begin/end), which gives its average duration over
+the timed region for the roofline entry.  A further, untimed pass records
+events at every stage boundary for the per-stage breakdown ("stages_ms";
+each boundary event adds a few microseconds there).
 
 The CPU baseline times the fp64 oracle on the host on a bounded sample of the
 same workload.
@@ -122,20 +124,30 @@ def run_workload(name, steps, warmup, binding, inputs, torch):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    binding.moe_ffn_profile_begin(steps)
+    # Timed region: events only around the w1/w3 kernel (each event costs a
+    # few microseconds of GPU time).
+    binding.moe_ffn_profile_begin(steps, ["gemm1_swiglu"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    stage_ms, calls = binding.moe_ffn_profile_end()
+    timed_ms, calls = binding.moe_ffn_profile_end()
     assert calls == steps, (calls, steps)
-    stage_avg = {kk: v / calls for kk, v in stage_ms.items()}
     ms_per_step = 1e3 * elapsed / steps
+    # Untimed breakdown pass: events at every stage boundary.
+    n_bd = min(steps, 10)
+    binding.moe_ffn_profile_begin(n_bd)
+    for _ in range(n_bd):
+        step()
+    torch.cuda.synchronize()
+    stage_ms, calls = binding.moe_ffn_profile_end()
+    stage_avg = {kk: v / calls for kk, v in stage_ms.items()}
+    stage_avg.pop("sum_splits", None)  # not launched by the timed calls
 
     g_bytes, g_flops = gemm1_algorithmic(wl, counts_h)
-    g_ms = stage_avg["gemm1_swiglu"]
+    g_ms = timed_ms["gemm1_swiglu"] / steps
     l_flops, l_bytes = layer_algorithmic(wl, counts_h)
     res = {
         "workload": name,
@@ -143,7 +155,7 @@ def run_workload(name, steps, warmup, binding, inputs, torch):
         "inp": inp,
         "ms_per_step": ms_per_step,
         "tokens_per_s": wl.T / (ms_per_step * 1e-3),
-        "stage_ms": {kk: round(v, 5) for kk, v in stage_avg.items()},
+        "stage_ms": {kk: round(v, 5) for kk, v in stage_avg.items()},  # breakdown pass
         "counts": counts_h.tolist(),
         "gemm1_ms": g_ms,
         "gemm1_gbs": g_bytes / (g_ms * 1e-3) / 1e9,

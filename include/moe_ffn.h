@@ -137,16 +137,21 @@ moe_status_t moe_rmsnorm(const void *h, void *x, int64_t T, int64_t d, float eps
 /*
  * Per-stage timing with HIP events, for benchmarks and tools.  Between
  * moe_ffn_profile_begin and moe_ffn_profile_end, the first max_calls forward
- * calls (any entry point, any stream) record an event at each stage boundary
- * on their own stream.  moe_ffn_profile_end waits for those events and writes
- * the summed milliseconds of each stage over the recorded calls into
- * stage_ms[MOE_NUM_STAGES] and the number of recorded calls into *calls.
- * Stages, in launch order: 0 router_topk, 1 route_scan, 2 gather_rows,
- * 3 gemm1_swiglu, 4 gemm2, 5 sum_splits (0 ms unless y_out is asked for),
- * 6 combine.  Not for concurrent use from several host threads.
+ * calls (any entry point, any stream) record an event on their own stream at
+ * the start and at the end of each stage whose bit (1 << stage) is set in
+ * stage_mask (0 means every stage).  Each recorded event costs a few
+ * microseconds of GPU time, so a timing run should ask only for the stages it
+ * needs.  moe_ffn_profile_end waits for those events and writes the summed
+ * milliseconds of each stage over the recorded calls into
+ * stage_ms[MOE_NUM_STAGES] (-1 for stages not in the mask) and the number of
+ * recorded calls into *calls.  Stages, in launch order: 0 router_topk,
+ * 1 route_scan, 2 gather_rows, 3 gemm1_swiglu, 4 gemm2, 5 sum_splits (runs
+ * only when y_out is asked for), 6 combine.  max_calls must be in [1, 1e6];
+ * a second begin before end, or an end without begin, is MOE_ERR_INVALID_ARG.
+ * Not for concurrent use from several host threads.
  */
 #define MOE_NUM_STAGES 7
-moe_status_t moe_ffn_profile_begin(int32_t max_calls);
+moe_status_t moe_ffn_profile_begin(int32_t max_calls, uint32_t stage_mask);
 moe_status_t moe_ffn_profile_end(float *stage_ms, int32_t *calls);
 const char *moe_ffn_stage_name(int32_t stage);
 

@@ -72,7 +72,7 @@ lib.moe_ffn_last_error.argtypes = []
 lib.moe_ffn_last_error.restype = ctypes.c_char_p
 lib.moe_ffn_release_workspace.argtypes = []
 lib.moe_ffn_release_workspace.restype = None
-lib.moe_ffn_profile_begin.argtypes = [ctypes.c_int32]
+lib.moe_ffn_profile_begin.argtypes = [ctypes.c_int32, ctypes.c_uint32]
 lib.moe_ffn_profile_begin.restype = ctypes.c_int
 lib.moe_ffn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
 lib.moe_ffn_profile_end.restype = ctypes.c_int
@@ -206,16 +206,24 @@ def moe_ffn_version() -> str:
     return lib.moe_ffn_version().decode()
 
 
-def moe_ffn_profile_begin(max_calls: int) -> None:
-    _check(lib.moe_ffn_profile_begin(max_calls))
+def moe_ffn_profile_begin(max_calls: int, stages=None) -> None:
+    """Time the given stages (names or indices; None = all) of the next
+    max_calls forward calls."""
+    mask = 0
+    for s in stages or ():
+        i = s if isinstance(s, int) else [moe_ffn_stage_name(j) for j in range(MOE_NUM_STAGES)].index(s)
+        mask |= 1 << i
+    _check(lib.moe_ffn_profile_begin(max_calls, mask))
 
 
 def moe_ffn_profile_end():
-    """Returns ({stage name: summed ms}, number of recorded calls)."""
+    """Returns ({stage name: summed ms} for the timed stages, number of
+    recorded calls)."""
     ms = (ctypes.c_float * MOE_NUM_STAGES)()
     calls = ctypes.c_int32(0)
     _check(lib.moe_ffn_profile_end(ms, ctypes.byref(calls)))
-    return {moe_ffn_stage_name(i): float(ms[i]) for i in range(MOE_NUM_STAGES)}, int(calls.value)
+    return ({moe_ffn_stage_name(i): float(ms[i]) for i in range(MOE_NUM_STAGES) if ms[i] >= 0},
+            int(calls.value))
 
 
 def moe_ffn_stage_name(i: int) -> str:

@@ -182,16 +182,26 @@ struct Profiler {
     bool active = false;
     int max_calls = 0;
     int calls = 0;
+    uint32_t mask = 0;         // stages timed
     hipEvent_t* ev = nullptr;  // [max_calls][MOE_NUM_STAGES + 1]
 };
 std::mutex g_prof_mu;
 Profiler g_prof;
 
-// Events for the next profiled call, or nullptr.
-hipEvent_t* profile_slot() {
+// Events for the next profiled call (nullptr if none) and the stage mask.
+hipEvent_t* profile_slot(uint32_t* mask) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof.active || g_prof.calls >= g_prof.max_calls) return nullptr;
+    *mask = g_prof.mask;
     return g_prof.ev + (size_t)(g_prof.calls++) * (MOE_NUM_STAGES + 1);
+}
+
+// Boundary i (the start of stage i, the end of stage i - 1) is recorded when
+// either neighbouring stage is timed.
+bool boundary_needed(uint32_t mask, int i) {
+    const bool after = i < MOE_NUM_STAGES && ((mask >> i) & 1u);
+    const bool before = i > 0 && ((mask >> (i - 1)) & 1u);
+    return after || before;
 }
 
 #define LAUNCH(call, name)                                   \
@@ -245,9 +255,10 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     const float* bias = opts ? opts->router_bias : nullptr;
     const void* residual = opts ? opts->residual : nullptr;
 
-    hipEvent_t* ev = profile_slot();
+    uint32_t prof_mask = 0;
+    hipEvent_t* ev = profile_slot(&prof_mask);
     auto mark = [&](int i) {
-        if (ev) (void)hipEventRecord(ev[i], stream);
+        if (ev && boundary_needed(prof_mask, i)) (void)hipEventRecord(ev[i], stream);
     };
     mark(0);
     LAUNCH(launch_router_topk(dtype, x, w_router, bias, Ti, di, Ei, ki, ids, gates, stream), "router_topk");
@@ -333,7 +344,7 @@ moe_status_t moe_rmsnorm(const void* h, void* x, int64_t T, int64_t d, float eps
     return MOE_OK;
 }
 
-moe_status_t moe_ffn_profile_begin(int32_t max_calls) {
+moe_status_t moe_ffn_profile_begin(int32_t max_calls, uint32_t stage_mask) {
     if (max_calls < 1 || max_calls > 1000000)
         return fail(MOE_ERR_INVALID_ARG, "max_calls must be in [1, 1e6]");
     std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -351,6 +362,7 @@ moe_status_t moe_ffn_profile_begin(int32_t max_calls) {
     g_prof.ev = ev;
     g_prof.max_calls = max_calls;
     g_prof.calls = 0;
+    g_prof.mask = stage_mask == 0 ? (1u << MOE_NUM_STAGES) - 1 : stage_mask & ((1u << MOE_NUM_STAGES) - 1);
     g_prof.active = true;
     return MOE_OK;
 }
@@ -362,9 +374,10 @@ moe_status_t moe_ffn_profile_end(float* stage_ms, int32_t* calls) {
     float sums[MOE_NUM_STAGES] = {0};
     for (int c = 0; c < g_prof.calls && st == MOE_OK; ++c) {
         hipEvent_t* e = g_prof.ev + (size_t)c * (MOE_NUM_STAGES + 1);
-        hipError_t r = hipEventSynchronize(e[MOE_NUM_STAGES]);
-        if (r != hipSuccess) { st = hip_fail(r, "hipEventSynchronize"); break; }
         for (int s = 0; s < MOE_NUM_STAGES; ++s) {
+            if (!((g_prof.mask >> s) & 1u)) continue;
+            hipError_t r = hipEventSynchronize(e[s + 1]);
+            if (r != hipSuccess) { st = hip_fail(r, "hipEventSynchronize"); break; }
             float ms = 0.0f;
             r = hipEventElapsedTime(&ms, e[s], e[s + 1]);
             if (r != hipSuccess) { st = hip_fail(r, "hipEventElapsedTime"); break; }
@@ -375,9 +388,11 @@ moe_status_t moe_ffn_profile_end(float* stage_ms, int32_t* calls) {
     for (size_t i = 0; i < n; ++i) (void)hipEventDestroy(g_prof.ev[i]);
     delete[] g_prof.ev;
     const int recorded = g_prof.calls;
+    const uint32_t mask = g_prof.mask;
     g_prof = Profiler();
     if (st != MOE_OK) return st;
-    if (stage_ms) for (int s = 0; s < MOE_NUM_STAGES; ++s) stage_ms[s] = sums[s];
+    if (stage_ms)
+        for (int s = 0; s < MOE_NUM_STAGES; ++s) stage_ms[s] = ((mask >> s) & 1u) ? sums[s] : -1.0f;
     if (calls) *calls = recorded;
     return MOE_OK;
 }

@@ -58,7 +58,6 @@ constexpr int kThreads = 256;
 constexpr int kBM = 256;
 constexpr int kBK = 32;
 constexpr int kCols = 256;                             // weight columns staged per step
-constexpr int kStages = 4;
 constexpr int kAUnits = kBM * kBK / 8;                 // 1024 16-byte units
 constexpr int kBUnits = kBK * kCols / 8;               // 1024 16-byte units
 constexpr int kStageBytes = (kAUnits + kBUnits) * 16;  // 32 KiB
