@@ -170,6 +170,71 @@ def run_workload(name, steps, warmup, binding, inputs, torch):
     return res
 
 
+def run_stack(steps, warmup, binding, inputs, torch):
+    """The 32-block stack h <- h + MoE(RMSNorm(h)) at T=2048 with all layers'
+    weights resident.  A step restores h0 (one 16 MiB copy) and runs the 32
+    blocks (RMSNorm + layer with the residual added in the combine)."""
+    wl = inputs.WORKLOADS["stack"]
+    layers = [inputs.make_weights(wl.d, wl.f, wl.E, torch.bfloat16, "cuda", 0, "stack", layer)
+              for layer in range(wl.layers)]
+    h0 = inputs.make_x(wl.T, wl.d, torch.bfloat16, "cuda", wl.x_dist, 0, "stack")
+    h = torch.empty_like(h0)
+    x = torch.empty_like(h0)
+    counts = [torch.zeros(wl.E, dtype=torch.int32, device="cuda") for _ in layers]
+    torch.cuda.synchronize()
+    log("[bench] stack: %d layers resident (%.1f GB of expert weights)"
+        % (len(layers), sum(w["w1"].numel() * 3 * 2 for w in layers) / 1e9))
+
+    def step(with_counts=False):
+        h.copy_(h0)
+        for i, w in enumerate(layers):
+            binding.moe_rmsnorm(h, x, eps=wl.rms_eps)
+            binding.moe_ffn_forward_ex(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=h,
+                                       residual=h,
+                                       expert_counts=counts[i] if with_counts else None)
+
+    step(with_counts=True)
+    torch.cuda.synchronize()
+    active = [int((c > 0).sum().item()) for c in counts]
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.moe_ffn_profile_begin(steps * wl.layers, ["gemm1_swiglu"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timed_ms, calls = binding.moe_ffn_profile_end()
+    assert calls == steps * wl.layers, (calls, steps)
+    ms_per_step = 1e3 * elapsed / steps
+    g_ms = timed_ms["gemm1_swiglu"] / calls
+    R = wl.T * wl.k
+    g_flops = 4.0 * R * wl.d * wl.f
+    flops = wl.layers * wl.T * (2.0 * wl.d * wl.E + wl.k * 6.0 * wl.d * wl.f)
+    nbytes = sum(a * 3 * wl.d * wl.f * 2 for a in active)
+    res = {
+        "workload": "stack (T=%d, %d layers, d=%d, f=%d, E=%d, k=%d)"
+                    % (wl.T, wl.layers, wl.d, wl.f, wl.E, wl.k),
+        "value": round(wl.T / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_layer": round(ms_per_step / wl.layers, 5),
+        "roofline": {"kernel": "gemm1_swiglu", "bound": "mfma",
+                     "achieved": round(g_flops / (g_ms * 1e-3) / 1e12, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "avg_launch_ms": round(g_ms, 5), "traffic": None},
+        "layer": {"tflops_active": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                  "hbm_gbs": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1)},
+    }
+    log("[bench] stack: %.3f ms/step (%.4f ms/layer), %.0f tokens/s"
+        % (ms_per_step, ms_per_step / wl.layers, res["value"]))
+    del layers
+    return res
+
+
 def roofline(res, bound):
     if bound == "hbm":
         achieved = res["gemm1_gbs"]
@@ -355,6 +420,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed"])
     ap.add_argument("--secondary", default="prefill", choices=["prefill", "decode", "skewed", "none"])
+    ap.add_argument("--stack", default="on", choices=["on", "off"],
+                    help="also time the 32-block stack (90 GB of weights resident)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -423,6 +490,13 @@ def main():
             "stages_ms": sec["stage_ms"],
         }
         prim["inp"] = prim_inp
+    if args.stack == "on":
+        prim_inp = prim.pop("inp")
+        del prim_inp
+        torch.cuda.empty_cache()
+        rec["stack"] = run_stack(max(2, args.steps // 4), 1, binding, inputs, torch)
+        torch.cuda.empty_cache()
+        prim["inp"] = inputs.workload_inputs(args.workload, "cuda")
     if args.calibrate_copy:
         calibrate_copy(torch)
     if args.no_cpu_baseline:

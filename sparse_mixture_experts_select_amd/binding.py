@@ -160,17 +160,29 @@ def moe_ffn_forward_ex(x, w_router, w1, w3, w2, k, out=None, stream=None, *, rou
     T, d, f, E = _shapes(x, w_router, w1, w3, w2)
     if out is None:
         out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like x")
+    R = T * k
+    i32, f32 = torch.int32, torch.float32
+    # (tensor, element count, dtype) the library reads or writes for each option
+    spec = {
+        "router_bias": (router_bias, E, f32), "topk_ids": (topk_ids, R, i32),
+        "topk_weights": (topk_weights, R, f32), "expert_counts": (expert_counts, E, i32),
+        "expert_offsets": (expert_offsets, E + 1, i32), "row_token": (row_token, R, i32),
+        "slot_row": (slot_row, R, i32), "h_out": (h_out, R * f, x.dtype),
+        "y_out": (y_out, R * d, f32), "residual": (residual, T * d, x.dtype),
+    }
     opts = MoeFfnOpts()
     opts.dtype = _dtype_code(x.dtype)
-    opts.router_bias = None if router_bias is None else router_bias.data_ptr()
-    for name, t in (("topk_ids", topk_ids), ("topk_weights", topk_weights),
-                    ("expert_counts", expert_counts), ("expert_offsets", expert_offsets),
-                    ("row_token", row_token), ("slot_row", slot_row), ("h_out", h_out),
-                    ("y_out", y_out), ("residual", residual)):
-        if t is not None:
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError("%s must be a contiguous GPU tensor" % name)
-            setattr(opts, name, t.data_ptr())
+    for name, (t, n, dt) in spec.items():
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+        if t.numel() != n or t.dtype != dt:
+            raise ValueError("%s must hold %d elements of %s (got %d of %s)"
+                             % (name, n, dt, t.numel(), t.dtype))
+        setattr(opts, name, t.data_ptr())
     if workspace is not None:
         opts.workspace = workspace.data_ptr()
         opts.workspace_bytes = workspace.numel() * workspace.element_size()

@@ -194,3 +194,50 @@ def test_skewed_workload():
     share = counts / counts.sum()
     print("near ties", r["near_ties"], "err", r["err_out"], "shares", np.round(share, 3))
     assert 0.35 < share[0] < 0.48
+
+
+def test_stack_workload_teacher_forced():
+    """32 blocks h <- h + MoE(RMSNorm(h)), T=2048, each with its own weights.
+    Every layer is checked on the GPU's own bf16 input of that layer: RMSNorm
+    and the output on sampled tokens, routing on every token."""
+    from sparse_mixture_experts_select_amd import binding
+    wl = inputs.WORKLOADS["stack"]
+    T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
+    banner("stack bf16 T=%d, %d layers (teacher-forced per layer)" % (T, wl.layers))
+    h = inputs.make_x(T, d, torch.bfloat16, DEV, wl.x_dist, 0, "stack")
+    x = torch.empty_like(h)
+    rng = np.random.default_rng(3)
+    total_ties = 0
+    for layer in range(wl.layers):
+        inp = inputs.make_weights(d, f, E, torch.bfloat16, DEV, 0, "stack", layer)
+        binding.moe_rmsnorm(h, x, eps=wl.rms_eps)
+        inp["x"] = x
+        g = PT.run_gpu(inp, k, residual=h)
+        host = PT.host_inputs(inp)
+        tok = np.sort(rng.choice(T, size=6, replace=False))
+        # RMSNorm of this layer's input, against the oracle
+        h_tok = inputs.host_array(h[torch.as_tensor(tok, device=DEV)])
+        x_ref = oracle.rmsnorm(h_tok, wl.rms_eps)
+        x_err = np.abs(PT.out_f64(x[torch.as_tensor(tok, device=DEV)]) - x_ref).max()
+        assert x_err <= 2 ** -8 * np.abs(x_ref).max(), "layer %d rmsnorm error %g" % (layer, x_err)
+        # routing on every token
+        logits, o_ids, _ = oracle.route(host["x"], host["w_router"], k)
+        exempt, ref_g = PT.check_routing(g, logits, o_ids, k)
+        total_ties += int(exempt.sum())
+        # h + MoE(x) on the sampled tokens: the MoE part to the bf16 bar, plus
+        # one bf16 rounding of the residual sum
+        ids = PT.to_np(g["ids"])
+        ref = oracle.moe_tokens(host["x"], None, host["w1"], host["w3"], host["w2"], k, tokens=tok,
+                                forced_ids=ids[tok], forced_gates=ref_g[tok])
+        moe_ref = ref["out"]
+        want = PT.out_f64(h[torch.as_tensor(tok, device=DEV)]) + moe_ref
+        got = PT.out_f64(g["out"][torch.as_tensor(tok, device=DEV)])
+        bound = PT.TOL[torch.bfloat16] * np.abs(moe_ref).max() + 2.0 ** -8 * np.abs(want)
+        worst = (np.abs(got - want) - bound).max()
+        assert worst <= 0, "layer %d output outside the bar by %g" % (layer, worst)
+        rel = np.abs(got - want).max() / np.abs(moe_ref).max()
+        print("layer %2d: near ties %d, rmsnorm err %.2e, out err %.2e of max|moe|, max|h| %.2f"
+              % (layer, int(exempt.sum()), x_err, rel, np.abs(want).max()), flush=True)
+        h = g["out"]
+        del inp, host, g
+    print("stack: %d near-tie tokens over %d layers" % (total_ties, wl.layers))
