@@ -16,17 +16,18 @@
 // bytes land at the wave's LDS base + 16 l).  SGPR buffer descriptors over A
 // and the expert's weights; each lane's byte offset is fixed for the whole
 // loop and a wave-uniform offset advances per K step.  Four LDS stages of
-// 32 KiB; loads run three K steps ahead, always exactly three (past the end
-// the refills repeat the last step: valid addresses, never read), so one
-// fixed wait, vmcnt(16), leaves each step's own loads complete.  No register
-// holds staged data and no VALU work is spent on it.  After that wait, one
-// barrier per step publishes the stage to all waves and frees the stage read
-// in the previous step; it is a raw s_barrier after lgkmcnt(0), between
-// compiler-only fences, so loads of later steps stay in flight across it.
-// Each stage is its own LDS array and the K loop is unrolled by four, so every
-// read and every refill names a fixed array; where the compiler can see that a
-// read does not depend on the refills in flight it adds no wait of its own.
-//
+// 32 KiB, loads three K steps ahead.  The one barrier of a step sits half
+// way through its MFMAs: before it each wave waits for its own loads of the
+// next stage (always exactly vmcnt(8): past the end the refills repeat the
+// last step, valid addresses never read); after it the wave refills the
+// stage of the previous step and reads the next step's A fragments under the
+// second half of the MFMAs, so a step starts with its operands in registers.
+// No register holds staged data and no VALU work is spent on it.  The
+// barrier is a raw s_barrier between compiler-only fences, so loads of later
+// steps stay in flight across it.  Each stage is its own LDS array and the K
+// loop is unrolled by four, so every read and every refill names a fixed
+// array, and the compiler's own waits for the DMA stay per stage.
+
 // LDS layouts (both bank-conflict free for the fragment reads):
 //   A stage: [256 rows][32 k], 64 bytes per row; the row's four 16-byte
 //     chunks are stored XOR (row/4)%4, so 16 rows x one chunk cover 256 bytes.
@@ -75,10 +76,10 @@ __device__ __forceinline__ int b_group_swz(int k) { return (k & 3) | (((k >> 3) 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
 #define MOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | (((n) >> 4) << 14))
 
-// Barrier between K steps: this wave's LDS reads are complete (lgkmcnt(0)),
-// so the stage it read last can be refilled once every wave has arrived; the
-// compiler-only fences keep memory accesses from moving across it, and DMA
-// loads of later steps stay in flight.
+// Barrier inside each K step: this wave's LDS reads are complete
+// (lgkmcnt(0)), so the stage it read in the previous step can be refilled
+// once every wave has arrived; the compiler-only fences keep memory accesses
+// from moving across it, and DMA loads of later steps stay in flight.
 __device__ __forceinline__ void stage_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -222,50 +223,92 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
                                                      16, b_voff[i_], kb_, 0, 0);            \
     } while (0)
 
-    // One K step on stage array CUR_: refill NEXT_ (the stage read in the
-    // previous step) with step kt + 3, then read CUR_'s fragments and run the
-    // MFMAs, one B fragment at a time.
-#define MOE_STEP(CUR_, NEXT_)                                                               \
-    if (kt < kt1) {                                                                         \
-        MOE_WAIT_VM(16);                                                                    \
-        stage_barrier();                                                                    \
-        MOE_ISSUE_STAGE(min(kt + 3, kt1 - 1), NEXT_);                                       \
-        const lds_char* st_ = (const lds_char*)(lds_void*)(CUR_);                           \
-        bf16x8 af_[8];                                                                      \
+#define MOE_READ_A(ST_, M_)                                                                 \
+    (*reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(                    \
+        (const lds_char*)(lds_void*)(ST_) + a_frag + (M_) * 16 * 64))
+
+#define MOE_B_GROUP(ST_, N_)                                                                \
+    {                                                                                       \
+        const short4_t lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                       \
+            (lds_short4*)((ST_) + b_frag[N_]));                                             \
+        const short4_t hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                       \
+            (lds_short4*)((ST_) + b_frag[N_] + 4 * 256));                                   \
+        const bf16x8 bf_ = __builtin_bit_cast(                                              \
+            bf16x8, __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7));             \
         _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_)                                    \
-            af_[m_] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(   \
-                st_ + a_frag + m_ * 16 * 64);                                               \
-        _Pragma("unroll") for (int n_ = 0; n_ < 8; ++n_) {                                  \
-            const short4_t lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                   \
-                (lds_short4*)(st_ + b_frag[n_]));                                           \
-            const short4_t hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                   \
-                (lds_short4*)(st_ + b_frag[n_] + 4 * 256));                                 \
-            const bf16x8 bf_ = __builtin_bit_cast(                                          \
-                bf16x8, __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7));         \
-            _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_)                                \
-                acc[m_][n_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af_[m_], bf_,         \
-                                                                      acc[m_][n_], 0, 0, 0); \
+            acc[m_][N_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m_], bf_,              \
+                                                                  acc[m_][N_], 0, 0, 0);    \
+    }
+
+    // One K step on stage CUR_, whose A fragments are already in af[].  For
+    // each B fragment n: two transposing reads, then 8 MFMAs.  Half way
+    // (before fragment 4): wait until this wave's loads of the next stage
+    // NXT_ are complete (vmcnt(8): only the stage after it may still be in
+    // flight), barrier (now every wave's loads of NXT_ have landed, and every
+    // wave has consumed its reads of REF_, the stage of the previous step),
+    // refill REF_ with step kt + 3, and read the next step's A fragments from
+    // NXT_ two at a time under the remaining MFMAs.
+    // A step past the end of the slice (the last loop iteration may hold up
+    // to three) skips its reads and MFMAs but still waits, takes the barrier
+    // and issues its (repeated, never read) refill, so every path through the
+    // loop issues the same sequence of DMA loads: the compiler's DMA wait
+    // tracking then stays per stage across the guards' control-flow merges.
+#define MOE_STEP(CUR_, NXT_, REF_)                                                          \
+    {                                                                                       \
+        const lds_char* st_ = (const lds_char*)(lds_void*)(CUR_);                           \
+        const bool live_ = kt < kt1;                                                        \
+        if (live_) {                                                                        \
+            MOE_B_GROUP(st_, 0)                                                             \
+            MOE_B_GROUP(st_, 1)                                                             \
+            MOE_B_GROUP(st_, 2)                                                             \
+            MOE_B_GROUP(st_, 3)                                                             \
+        }                                                                                   \
+        MOE_WAIT_VM(8);                                                                     \
+        stage_barrier();                                                                    \
+        MOE_ISSUE_STAGE(min(kt + 3, kt1 - 1), REF_);                                        \
+        if (live_) {                                                                        \
+            bf16x8 an[8];                                                                   \
+            an[0] = MOE_READ_A(NXT_, 0);                                                    \
+            an[1] = MOE_READ_A(NXT_, 1);                                                    \
+            MOE_B_GROUP(st_, 4)                                                             \
+            an[2] = MOE_READ_A(NXT_, 2);                                                    \
+            an[3] = MOE_READ_A(NXT_, 3);                                                    \
+            MOE_B_GROUP(st_, 5)                                                             \
+            an[4] = MOE_READ_A(NXT_, 4);                                                    \
+            an[5] = MOE_READ_A(NXT_, 5);                                                    \
+            MOE_B_GROUP(st_, 6)                                                             \
+            an[6] = MOE_READ_A(NXT_, 6);                                                    \
+            an[7] = MOE_READ_A(NXT_, 7);                                                    \
+            MOE_B_GROUP(st_, 7)                                                             \
+            _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_) af[m_] = an[m_];               \
         }                                                                                   \
         ++kt;                                                                               \
     }
 
     // Loads in flight: the prologue fills st0, st1, st2 with steps kt0,
-    // kt0+1, kt0+2; each step refills one stage, so exactly three younger
-    // steps are in flight at every step's wait and one fixed vmcnt(16) leaves
-    // the step's own loads complete.  Past the last step the refills repeat it
-    // (valid addresses, never read).
+    // kt0+1, kt0+2 and waits for the first; each step refills one stage half
+    // way through, so at every half-way wait exactly two younger steps are in
+    // flight and one fixed vmcnt(8) leaves the next step's loads complete.
+    // Past the last step the refills repeat it (valid addresses, never read).
     int kt = kt0;
     if (kt0 < kt1) {
         MOE_ISSUE_STAGE(kt0, st0);
         MOE_ISSUE_STAGE(min(kt0 + 1, kt1 - 1), st1);
         MOE_ISSUE_STAGE(min(kt0 + 2, kt1 - 1), st2);
+        MOE_WAIT_VM(16);
+        stage_barrier();
+        bf16x8 af[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) af[m] = MOE_READ_A(st0, m);
         while (kt < kt1) {
-            MOE_STEP(st0, st3)
-            MOE_STEP(st1, st0)
-            MOE_STEP(st2, st1)
-            MOE_STEP(st3, st2)
+            MOE_STEP(st0, st1, st3)
+            MOE_STEP(st1, st2, st0)
+            MOE_STEP(st2, st3, st1)
+            MOE_STEP(st3, st0, st2)
         }
     }
+#undef MOE_B_GROUP
+#undef MOE_READ_A
 #undef MOE_STEP
 #undef MOE_ISSUE_STAGE
     // No load may still be writing LDS when the stages are reused below.
