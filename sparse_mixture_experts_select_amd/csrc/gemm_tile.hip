@@ -76,12 +76,12 @@ __device__ __forceinline__ int b_group_swz(int k) { return (k & 3) | (((k >> 3) 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
 #define MOE_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | (((n) >> 4) << 14))
 
-// Barrier inside each K step: this wave's LDS reads are complete
-// (lgkmcnt(0)), so the stage it read in the previous step can be refilled
-// once every wave has arrived; the compiler-only fences keep memory accesses
-// from moving across it, and DMA loads of later steps stay in flight.
+// Barrier inside each K step.  Every LDS read of the stage about to be
+// refilled was consumed by an MFMA of the previous step (so it has completed
+// and no count wait is needed here); the compiler-only fences keep memory
+// accesses from moving across the barrier, and DMA loads of later steps stay
+// in flight.
 __device__ __forceinline__ void stage_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -227,27 +227,37 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     (*reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(                    \
         (const lds_char*)(lds_void*)(ST_) + a_frag + (M_) * 16 * 64))
 
-#define MOE_B_GROUP(ST_, N_)                                                                \
-    {                                                                                       \
-        const short4_t lo_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                       \
-            (lds_short4*)((ST_) + b_frag[N_]));                                             \
-        const short4_t hi_ = __builtin_amdgcn_ds_read_tr16_b64_v4i16(                       \
-            (lds_short4*)((ST_) + b_frag[N_] + 4 * 256));                                   \
-        const bf16x8 bf_ = __builtin_bit_cast(                                              \
-            bf16x8, __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7));             \
-        _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_)                                    \
-            acc[m_][N_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m_], bf_,              \
-                                                                  acc[m_][N_], 0, 0, 0);    \
+#define MOE_READ_B(ST_, N_)                                                                 \
+    __builtin_bit_cast(bf16x8, __builtin_shufflevector(                                     \
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((ST_) + b_frag[N_])),        \
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((ST_) + b_frag[N_] + 4 * 256)), \
+        0, 1, 2, 3, 4, 5, 6, 7))
+
+#define MOE_MFMAS(N_, BF_)                                                                  \
+    _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_)                                        \
+        acc[m_][N_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m_], BF_, acc[m_][N_], 0, 0, 0)
+
+// Scheduling hints: within a group of 8 MFMAs, put one of the group's LDS
+// reads (for fragments two groups ahead) after each of the first NR_ MFMAs,
+// and NV_ of the stage refill's DMA loads after MFMAs 3 and 6, so the wave
+// never holds a burst of memory instructions while the matrix core idles.
+#define MOE_SCHED_GROUP(NR_, NV_)                                                           \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                      \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+        if (i_ < (NR_)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  \
+        if ((i_ == 2 && (NV_) > 0) || (i_ == 5 && (NV_) > 1))                               \
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                              \
     }
 
-    // One K step on stage CUR_, whose A fragments are already in af[].  For
-    // each B fragment n: two transposing reads, then 8 MFMAs.  Half way
-    // (before fragment 4): wait until this wave's loads of the next stage
-    // NXT_ are complete (vmcnt(8): only the stage after it may still be in
-    // flight), barrier (now every wave's loads of NXT_ have landed, and every
-    // wave has consumed its reads of REF_, the stage of the previous step),
-    // refill REF_ with step kt + 3, and read the next step's A fragments from
-    // NXT_ two at a time under the remaining MFMAs.
+    // One K step on stage CUR_.  On entry af[] holds its A fragments and
+    // bq0, bq1 its first two B fragments; B fragment n + 2 is read while the
+    // MFMAs of fragment n run.  Half way (before fragment 4): wait until this
+    // wave's loads of the next stage NXT_ are complete (vmcnt(8): only the
+    // stage after it may still be in flight), barrier (now every wave's loads
+    // of NXT_ have landed, and every wave has consumed its reads of REF_, the
+    // stage of the previous step), refill REF_ with step kt + 3, and read the
+    // next step's A fragments and first two B fragments from NXT_ under the
+    // remaining MFMAs.
     // A step past the end of the slice (the last loop iteration may hold up
     // to three) skips its reads and MFMAs but still waits, takes the barrier
     // and issues its (repeated, never read) refill, so every path through the
@@ -257,29 +267,47 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     {                                                                                       \
         const lds_char* st_ = (const lds_char*)(lds_void*)(CUR_);                           \
         const bool live_ = kt < kt1;                                                        \
+        bf16x8 b4_, b5_;                                                                    \
         if (live_) {                                                                        \
-            MOE_B_GROUP(st_, 0)                                                             \
-            MOE_B_GROUP(st_, 1)                                                             \
-            MOE_B_GROUP(st_, 2)                                                             \
-            MOE_B_GROUP(st_, 3)                                                             \
+            const bf16x8 b2_ = MOE_READ_B(st_, 2);                                          \
+            MOE_MFMAS(0, bq0);                                                              \
+            const bf16x8 b3_ = MOE_READ_B(st_, 3);                                          \
+            MOE_MFMAS(1, bq1);                                                              \
+            b4_ = MOE_READ_B(st_, 4);                                                       \
+            MOE_MFMAS(2, b2_);                                                              \
+            b5_ = MOE_READ_B(st_, 5);                                                       \
+            MOE_MFMAS(3, b3_);                                                              \
+            MOE_SCHED_GROUP(2, 0);                                                          \
+            MOE_SCHED_GROUP(2, 0);                                                          \
+            MOE_SCHED_GROUP(2, 0);                                                          \
+            MOE_SCHED_GROUP(2, 0);                                                          \
         }                                                                                   \
         MOE_WAIT_VM(8);                                                                     \
         stage_barrier();                                                                    \
         MOE_ISSUE_STAGE(min(kt + 3, kt1 - 1), REF_);                                        \
         if (live_) {                                                                        \
+            const lds_char* sn_ = (const lds_char*)(lds_void*)(NXT_);                       \
             bf16x8 an[8];                                                                   \
+            const bf16x8 b6_ = MOE_READ_B(st_, 6);                                          \
             an[0] = MOE_READ_A(NXT_, 0);                                                    \
             an[1] = MOE_READ_A(NXT_, 1);                                                    \
-            MOE_B_GROUP(st_, 4)                                                             \
+            MOE_MFMAS(4, b4_);                                                              \
+            const bf16x8 b7_ = MOE_READ_B(st_, 7);                                          \
             an[2] = MOE_READ_A(NXT_, 2);                                                    \
             an[3] = MOE_READ_A(NXT_, 3);                                                    \
-            MOE_B_GROUP(st_, 5)                                                             \
+            MOE_MFMAS(5, b5_);                                                              \
             an[4] = MOE_READ_A(NXT_, 4);                                                    \
             an[5] = MOE_READ_A(NXT_, 5);                                                    \
-            MOE_B_GROUP(st_, 6)                                                             \
             an[6] = MOE_READ_A(NXT_, 6);                                                    \
             an[7] = MOE_READ_A(NXT_, 7);                                                    \
-            MOE_B_GROUP(st_, 7)                                                             \
+            bq0 = MOE_READ_B(sn_, 0);                                                       \
+            MOE_MFMAS(6, b6_);                                                              \
+            bq1 = MOE_READ_B(sn_, 1);                                                       \
+            MOE_MFMAS(7, b7_);                                                              \
+            MOE_SCHED_GROUP(4, 2);                                                          \
+            MOE_SCHED_GROUP(4, 2);                                                          \
+            MOE_SCHED_GROUP(6, 2);                                                          \
+            MOE_SCHED_GROUP(2, 2);                                                          \
             _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_) af[m_] = an[m_];               \
         }                                                                                   \
         ++kt;                                                                               \
@@ -300,6 +328,9 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         bf16x8 af[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) af[m] = MOE_READ_A(st0, m);
+        const lds_char* s0_ = (const lds_char*)(lds_void*)st0;
+        bf16x8 bq0 = MOE_READ_B(s0_, 0);
+        bf16x8 bq1 = MOE_READ_B(s0_, 1);
         while (kt < kt1) {
             MOE_STEP(st0, st1, st3)
             MOE_STEP(st1, st2, st0)
@@ -307,7 +338,9 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
             MOE_STEP(st3, st0, st2)
         }
     }
-#undef MOE_B_GROUP
+#undef MOE_SCHED_GROUP
+#undef MOE_MFMAS
+#undef MOE_READ_B
 #undef MOE_READ_A
 #undef MOE_STEP
 #undef MOE_ISSUE_STAGE
