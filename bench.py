@@ -235,6 +235,49 @@ def run_stack(steps, warmup, binding, inputs, torch):
     return res
 
 
+SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384)
+
+
+def run_sweep(steps, warmup, binding, inputs, torch):
+    """Tokens/s and both roofline fractions of the layer at Mixtral shapes
+    over batch sizes T = 1 .. 16384 (one set of prefill-distributed weights,
+    unit-RMS tokens), locating the HBM-bound to MFMA-bound crossover."""
+    wl = inputs.WORKLOADS["prefill"]
+    w = inputs.make_weights(wl.d, wl.f, wl.E, torch.bfloat16, "cuda", 0, "prefill", 0)
+    rows = []
+    for T in SWEEP_T:
+        x = inputs.make_x(T, wl.d, torch.bfloat16, "cuda", "rms", 0, "sweep")
+        out = torch.empty_like(x)
+        counts = torch.zeros(wl.E, dtype=torch.int32, device="cuda")
+        binding.moe_ffn_forward_ex(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=out,
+                                   expert_counts=counts)
+        torch.cuda.synchronize()
+        active = int((counts > 0).sum().item())
+        n = max(steps, 5)
+        for _ in range(warmup):
+            binding.moe_ffn_forward(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=out)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            binding.moe_ffn_forward(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=out)
+        torch.cuda.synchronize()
+        ms = 1e3 * (time.perf_counter() - t0) / n
+        flops = T * (2.0 * wl.d * wl.E + wl.k * 6.0 * wl.d * wl.f)
+        nbytes = active * 3 * wl.d * wl.f * 2 + wl.d * wl.E * 2 + 2 * T * wl.d * 2
+        row = {"T": T, "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+               "active_experts": active,
+               "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+               "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+               "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        rows.append(row)
+        log("[sweep] T=%5d  %8.4f ms  %11.1f tokens/s  %7.1f TFLOP/s (%.3f)  %7.1f GB/s (%.3f)"
+            % (T, ms, row["tokens_per_s"], row["tflops"], row["mfma_frac"], row["hbm_gbs"],
+               row["hbm_frac"]))
+        del x, out
+    return rows
+
+
 def roofline(res, bound):
     if bound == "hbm":
         achieved = res["gemm1_gbs"]
@@ -422,6 +465,8 @@ def main():
     ap.add_argument("--secondary", default="prefill", choices=["prefill", "decode", "skewed", "none"])
     ap.add_argument("--stack", default="on", choices=["on", "off"],
                     help="also time the 32-block stack (90 GB of weights resident)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the layer over T = 1 .. 16384 (prefill weights)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -490,6 +535,13 @@ def main():
             "stages_ms": sec["stage_ms"],
         }
         prim["inp"] = prim_inp
+    if args.sweep:
+        prim_inp = prim.pop("inp")
+        del prim_inp
+        torch.cuda.empty_cache()
+        rec["sweep"] = run_sweep(args.steps, args.warmup, binding, inputs, torch)
+        torch.cuda.empty_cache()
+        prim["inp"] = inputs.workload_inputs(args.workload, "cuda")
     if args.stack == "on":
         prim_inp = prim.pop("inp")
         del prim_inp

@@ -46,6 +46,7 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 struct Plan {
     int variant = GEMM_LARGE_M;
     int splits = 1;
+    bool g1_ksplit = false;  // streamed GEMM 1: split K over the waves of a workgroup
     size_t ids = 0, gates = 0, counts = 0, offsets = 0, slot_row = 0, row_token = 0;
     size_t x_perm = 0, h = 0, y = 0, total = 0;
 };
@@ -64,6 +65,10 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
             int64_t mt = (R + 15) / 16;
             if (mt < busy_experts) mt = busy_experts;
             const int64_t tiles = nt2 * mt;
+            // GEMM 1 gives each wave a 128-column slab over all of K; when
+            // that leaves most CUs idle (one or two tokens), split K over the
+            // waves of a workgroup instead.
+            p.g1_ksplit = mt * ((f + 511) / 512) < 128;
             // GEMM 2 runs one slab per workgroup with the K range split over
             // its 4 waves; cut K further across workgroups only when that
             // leaves fewer than ~1000 waves streaming.
@@ -268,7 +273,8 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     LAUNCH(launch_gather_rows(dtype, x, row_token, R, di, x_perm, stream), "gather_rows");
     mark(3);
     if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM) {
-        LAUNCH(launch_gemm1_swiglu_stream(x_perm, w1, w3, offsets, R, Ei, di, fi, h, stream), "gemm1_swiglu");
+        LAUNCH(launch_gemm1_swiglu_stream(x_perm, w1, w3, offsets, R, Ei, di, fi, plan.g1_ksplit, h, stream),
+               "gemm1_swiglu");
         mark(4);
         LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");
     } else if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_TILE256) {

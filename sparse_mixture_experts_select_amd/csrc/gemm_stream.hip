@@ -9,7 +9,8 @@
 // workgroup shapes, both of 4 wavefronts:
 //   KSPLIT_WAVES: one slab; the 4 waves split the slice's K range into 4
 //                 contiguous quarters and add their partial sums in LDS once
-//                 at the end (used when there are few slabs, GEMM 2);
+//                 at the end (used when there are few slabs: GEMM 2, and
+//                 GEMM 1 when only a few experts hold rows);
 //   otherwise:    4 adjacent slabs, one per wave, each over the whole K range
 //                 (no reduction; fewer, longer-lived waves, GEMM 1).
 // Each wavefront streams its weight rows straight from HBM into registers:
@@ -204,8 +205,10 @@ hipError_t launch_stream(const void* A, const void* B0, const void* B1, void* C,
 }  // namespace
 
 hipError_t launch_gemm1_swiglu_stream(const void* x_perm, const void* w1, const void* w3,
-                                      const int32_t* offsets, int R, int E, int d, int f, void* h,
-                                      hipStream_t stream) {
+                                      const int32_t* offsets, int R, int E, int d, int f,
+                                      bool ksplit_waves, void* h, hipStream_t stream) {
+    if (ksplit_waves)
+        return launch_stream<true, true>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
     return launch_stream<true, false>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
 }
 

@@ -55,6 +55,7 @@ SMALL = [
     (48, 192, 320, 8, 2, torch.bfloat16),     # ragged slabs, experts above 16 rows, K split 2
     (20, 256, 1024, 8, 2, torch.bfloat16),    # K split 8, one step per wave
     (5, 128, 128, 64, 8, torch.bfloat16),     # E = 64, most experts empty
+    (2, 256, 1024, 8, 2, torch.bfloat16),     # GEMM 1 with K split over the waves
     (50, 100, 60, 5, 2, torch.float32),
     (200, 64, 96, 16, 4, torch.float32),
 ]
