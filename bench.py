@@ -45,7 +45,7 @@ GEMM1_KERNEL = {
 }
 CALIBRATION_BYTES = 1 << 30
 PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d gpurun_out/pmc_{tag} -o run -- "
-               "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy")
+               "python3 bench.py --steps 3 --warmup 1 --stack off --no-cpu-baseline --calibrate-copy")
 TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o run -- "
                  "python3 bench.py --steps 10 --warmup 2 --cpu-seconds 2")
 
@@ -347,11 +347,12 @@ def summarize_counters(fetch_dir, write_dir):
     rows = {"FETCH_SIZE": _counter_rows(fetch_dir), "WRITE_SIZE": _counter_rows(write_dir)}
     factor, calib = {}, {}
     for name, rs in rows.items():
-        vals = [float(r["Counter_Value"]) for r in rs
-                if r["Counter_Name"] == name and "copyBuffer" in r["Kernel_Name"]]
+        vals = sorted(float(r["Counter_Value"]) for r in rs
+                      if r["Counter_Name"] == name and "copyBuffer" in r["Kernel_Name"])
         if not vals:
             raise SystemExit("no calibration copy dispatches in the %s run" % name)
-        calib[name] = statistics.median(vals)
+        # the calibration copies are the three largest copies of the run
+        calib[name] = statistics.median(vals[-3:])
         factor[name] = CALIBRATION_BYTES / (calib[name] * 1024.0)
     written = []
     for wl, (src, pattern) in GEMM1_KERNEL.items():
@@ -423,7 +424,7 @@ def _short_kernel_name(name):
 
 def summarize_trace(trace_dir):
     """Condense the --kernel-trace output of TRACE_COMMAND into
-    profiles/moe_layer_decode_prefill_kernel_stats.txt: per kernel and grid
+    profiles/moe_layer_decode_prefill_stack_kernel_stats.txt: per kernel and grid
     size (which tells the decode launches from the prefill ones) the number of
     calls and the average / min / max duration."""
     import csv
@@ -438,10 +439,11 @@ def summarize_trace(trace_dir):
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         g = groups.setdefault(key, {"d": [], "first": int(r["Dispatch_Id"]), "row": r})
         g["d"].append(dur)
-    out = os.path.join(ROOT, "profiles", "moe_layer_decode_prefill_kernel_stats.txt")
+    out = os.path.join(ROOT, "profiles", "moe_layer_decode_prefill_stack_kernel_stats.txt")
     with open(out, "w") as fh:
-        fh.write("# rocprofv3 kernel trace of the benchmark: decode (T=32), then prefill "
-                 "(T=4096); d=4096 f=14336 E=8 k=2 bf16\n")
+        fh.write("# rocprofv3 kernel trace of the benchmark: decode (T=32), prefill (T=4096), "
+                 "then the 32-block stack (T=2048; rmsnorm + layer per block); d=4096 f=14336 "
+                 "E=8 k=2 bf16\n")
         fh.write("# command: %s\n" % TRACE_COMMAND)
         fh.write("# summarized by: python3 bench.py --summarize-trace gpurun_out/trace\n")
         fh.write("# calls = warm-up + one routing probe call + timed steps; durations in us; "
