@@ -79,7 +79,10 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
             if (s > smax) s = smax;
             if (s < 1) s = 1;
             p.splits = (int)s;
-        } else if (R >= 128 * E) {
+        } else if (R >= 128 * E && R * (d > f ? d : f) * 2 < ((int64_t)1 << 31) &&
+                   d * f * 2 < ((int64_t)1 << 31)) {
+            // (the 256-row tile kernels address x_perm, h and each weight
+            // matrix with 32-bit buffer offsets: each must stay under 2 GiB)
             // Many rows per expert: 256x256 macro tiles.  GEMM 2 has d/256
             // column tiles; when that gives under ~4 workgroups per CU, cut
             // its K range in two (partials summed by the combine).
@@ -270,7 +273,10 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     mark(1);
     LAUNCH(launch_route_scan(ids, Ti, ki, Ei, counts, offsets, slot_row, row_token, stream), "route_scan");
     mark(2);
-    LAUNCH(launch_gather_rows(dtype, x, row_token, R, di, x_perm, stream), "gather_rows");
+    // The 256-row tile GEMMs read x_perm and h in a K-blocked layout (see
+    // gemm_tile.hip); a caller asking for h gets it row-major instead.
+    const int kb = (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_TILE256 && !(opts && opts->h_out)) ? 1 : 0;
+    LAUNCH(launch_gather_rows(dtype, x, row_token, R, di, kb, x_perm, stream), "gather_rows");
     mark(3);
     if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM) {
         LAUNCH(launch_gemm1_swiglu_stream(x_perm, w1, w3, offsets, R, Ei, di, fi, plan.g1_ksplit, h, stream),
@@ -278,9 +284,9 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
         mark(4);
         LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");
     } else if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_TILE256) {
-        LAUNCH(launch_gemm1_swiglu_tile(x_perm, w1, w3, offsets, R, Ei, di, fi, h, stream), "gemm1_swiglu");
+        LAUNCH(launch_gemm1_swiglu_tile(x_perm, w1, w3, offsets, R, Ei, di, fi, kb, h, stream), "gemm1_swiglu");
         mark(4);
-        LAUNCH(launch_gemm2_tile(h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");
+        LAUNCH(launch_gemm2_tile(h, w2, offsets, R, Ei, fi, di, plan.splits, kb, y, stream), "gemm2");
     } else if (dtype == MOE_DTYPE_BF16) {
         LAUNCH(launch_gemm1_swiglu_bf16(plan.variant, x_perm, w1, w3, offsets, R, Ei, di, fi, h, stream), "gemm1_swiglu");
         mark(4);

@@ -39,8 +39,9 @@ hipError_t launch_route_scan(const int32_t* ids, int T, int k, int E, int32_t* c
                              int32_t* offsets, int32_t* slot_row, int32_t* row_token,
                              hipStream_t stream);
 
+// kb: write x_perm in the K-blocked layout of the 256-row tile GEMM (bf16)
 hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token, int R, int d,
-                              void* x_perm, hipStream_t stream);
+                              int kb, void* x_perm, hipStream_t stream);
 
 // Grouped GEMM 1 with the SwiGLU epilogue: for each grouped row r of expert e,
 // h[r,:] = SiLU(x_perm[r,:] . w1[e]) * (x_perm[r,:] . w3[e]).
@@ -69,11 +70,13 @@ hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* off
 
 // The same two contractions for batches with many rows per expert: 256x256
 // macro tiles, double-buffered LDS.
+// kb: A (x_perm) and the h output in the K-blocked layout
 hipError_t launch_gemm1_swiglu_tile(const void* x_perm, const void* w1, const void* w3,
-                                    const int32_t* offsets, int R, int E, int d, int f, void* h,
-                                    hipStream_t stream);
+                                    const int32_t* offsets, int R, int E, int d, int f, int kb,
+                                    void* h, hipStream_t stream);
+// kb: A (h) in the K-blocked layout
 hipError_t launch_gemm2_tile(const void* h, const void* w2, const int32_t* offsets, int R, int E,
-                             int f, int d, int splits, float* y, hipStream_t stream);
+                             int f, int d, int splits, int kb, float* y, hipStream_t stream);
 
 // out[t,:] = (residual[t,:] +) sum_j gates[t,j] * sum_s y[s][slot_row[t*k+j], :]
 hipError_t launch_combine(int dtype, const float* y, int splits, const float* gates,

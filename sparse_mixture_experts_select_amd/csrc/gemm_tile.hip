@@ -30,7 +30,10 @@
 
 // LDS layouts (both bank-conflict free for the fragment reads):
 //   A stage: [256 rows][32 k], 64 bytes per row; the row's four 16-byte
-//     chunks are stored XOR (row/4)%4, so 16 rows x one chunk cover 256 bytes.
+//     chunks are stored XOR (row/2)%4.  A fragment read (ds_read_b128, one
+//     16-byte chunk per lane, 16 rows) then spreads over all 64 banks; the
+//     plain row order, or an XOR with (row/4)%4, leaves it 2-way conflicted
+//     (measured: half the read rate).
 //   B stage: two halves of [32 k][128 n] (GEMM 1: w1 | w3; GEMM 2: columns
 //     0..127 | 128..255), the weights' own orientation (n contiguous), 256
 //     bytes per k row in 32-byte groups of 16 columns; group G of row k is
@@ -91,7 +94,7 @@ template <bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
     void* __restrict__ C, const int32_t* __restrict__ offsets, int R, int E, int K, int N,
-    int splits) {
+    int splits, int kb) {
     constexpr int BN = DUAL ? 128 : 256;  // output columns per tile
     // One array per stage: the compiler can then tell the stage being read
     // from the stages the DMA is writing, and does not wait for those loads.
@@ -160,11 +163,14 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int u = 256 * i + 64 * wave + lane;
-        // A: row r = u/4; stored chunk u%4 holds logical chunk (u%4) ^ ((r/4)%4).
+        // A: row r = u/4; stored chunk u%4 holds logical chunk (u%4) ^ ((r/2)%4).
         const int r = u >> 2;
-        const int c = (u & 3) ^ ((r >> 2) & 3);
+        const int c = (u & 3) ^ ((r >> 1) & 3);
         const int grow = min(row0 + r, row_end - 1);  // rows past the expert only feed unstored rows
-        a_voff[i] = (grow * K + 8 * c) * 2;
+        // row-major A: row grow at grow * K; K-blocked A: block kt at kt * R * 32,
+        // row grow at grow * 32 within it (one K step of 256 rows is 16 KiB
+        // of contiguous memory, read in full 128-byte lines)
+        a_voff[i] = (kb ? grow * 32 + 8 * c : grow * K + 8 * c) * 2;
         // B: half h = u/512 (instructions 0,1 -> half 0, 2,3 -> half 1); within
         // the half, k row kk = (u%512)/16 and stored unit p = u%16 is group
         // (p/2) ^ swz(kk), 8-column piece p%2.
@@ -176,15 +182,15 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         if (gcol >= N) gcol = 0;  // columns past N only feed unstored columns
         b_voff[i] = (kk * N + gcol) * 2;
     }
-    const int a_step = kBK * 2;      // bytes per K step in A
+    const int a_step = kb ? R * kBK * 2 : kBK * 2;  // bytes per K step in A
     const int b_step = kBK * N * 2;  // bytes per K step in B
 
     // ---- fragment addressing (bytes within a stage)
     const int lrow = lane & 15;
     const int lgrp = lane >> 4;
     // A fragment m: row wm*128 + 16 m + lrow, chunk lgrp, stored at chunk
-    // lgrp ^ ((row/4)%4) = lgrp ^ ((lrow/4)%4) for every m.
-    const int a_frag = (wm * 128 + lrow) * 64 + 16 * (lgrp ^ ((lrow >> 2) & 3));
+    // lgrp ^ ((row/2)%4) = lgrp ^ ((lrow/2)%4) for every m.
+    const int a_frag = (wm * 128 + lrow) * 64 + 16 * (lgrp ^ ((lrow >> 1) & 3));
     // B fragment n: 16 columns of one half; lane (lgrp, lrow) addresses k row
     // 8 lgrp + lrow/4 (+4 for the second read), columns 4 (lrow%4) .. +3.
     const int b_k = 8 * lgrp + (lrow >> 2);
@@ -368,18 +374,38 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
                 }
         __syncthreads();
         uint16_t* h = reinterpret_cast<uint16_t*>(C);
+        if (kb) {
+            // K-blocked h: for each of the tile's 4 blocks of 32 columns, its
+            // 256 rows are one contiguous run of 64-byte row pieces.
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int idx = tid + kThreads * q;
-            const int row = idx >> 4;   // 0..255
-            const int ch = idx & 15;    // 16-byte chunk of the row
-            const int grow = row0 + row;
-            const int gc = col0 + ch * 8;
-            const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(row < 128 ? st0 : st1);
-            const int rr = row & 127;
-            if (grow < row_end && gc < N)
-                *reinterpret_cast<uint4*>(h + (size_t)grow * N + gc) =
-                    *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
+            for (int q = 0; q < 16; ++q) {
+                const int idx = tid + kThreads * q;
+                const int piece = idx & 3;        // 16-byte piece of the 64-byte row segment
+                const int row = (idx >> 2) & 255;
+                const int b = idx >> 10;          // block of 32 columns within the tile
+                const int ch = 4 * b + piece;     // 16-byte chunk of the staged row
+                const int grow = row0 + row;
+                const int gc = col0 + ch * 8;
+                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(row < 128 ? st0 : st1);
+                const int rr = row & 127;
+                if (grow < row_end && gc < N)
+                    *reinterpret_cast<uint4*>(h + ((size_t)(gc >> 5) * R + grow) * 32 + (gc & 31)) =
+                        *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int idx = tid + kThreads * q;
+                const int row = idx >> 4;   // 0..255
+                const int ch = idx & 15;    // 16-byte chunk of the row
+                const int grow = row0 + row;
+                const int gc = col0 + ch * 8;
+                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(row < 128 ? st0 : st1);
+                const int rr = row & 127;
+                if (grow < row_end && gc < N)
+                    *reinterpret_cast<uint4*>(h + (size_t)grow * N + gc) =
+                        *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
+            }
         }
     } else {
         float* y = reinterpret_cast<float*>(C) + (size_t)split * R * N;
@@ -400,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 
 template <bool DUAL>
 hipError_t launch_tile(const void* A, const void* B0, const void* B1, void* C,
-                       const int32_t* offsets, int R, int E, int K, int N, int splits,
+                       const int32_t* offsets, int R, int E, int K, int N, int splits, int kb,
                        hipStream_t stream) {
     const long long BN = DUAL ? 128 : 256;
     const long long NT = (N + BN - 1) / BN;
@@ -409,21 +435,21 @@ hipError_t launch_tile(const void* A, const void* B0, const void* B1, void* C,
     grid = (grid + 7) / 8 * 8;
     hipLaunchKernelGGL((tile_gemm_kernel<DUAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const bf16*>(A), reinterpret_cast<const bf16*>(B0),
-                       reinterpret_cast<const bf16*>(B1), C, offsets, R, E, K, N, splits);
+                       reinterpret_cast<const bf16*>(B1), C, offsets, R, E, K, N, splits, kb);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm1_swiglu_tile(const void* x_perm, const void* w1, const void* w3,
-                                    const int32_t* offsets, int R, int E, int d, int f, void* h,
-                                    hipStream_t stream) {
-    return launch_tile<true>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
+                                    const int32_t* offsets, int R, int E, int d, int f, int kb,
+                                    void* h, hipStream_t stream) {
+    return launch_tile<true>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, kb, stream);
 }
 
 hipError_t launch_gemm2_tile(const void* h, const void* w2, const int32_t* offsets, int R, int E,
-                             int f, int d, int splits, float* y, hipStream_t stream) {
-    return launch_tile<false>(h, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+                             int f, int d, int splits, int kb, float* y, hipStream_t stream) {
+    return launch_tile<false>(h, w2, nullptr, y, offsets, R, E, f, d, splits, kb, stream);
 }
 
 }  // namespace moe

@@ -117,6 +117,25 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
     }
 }
 
+// The same gather into the K-blocked layout of the 256-row tile GEMM:
+// element (r, i) of x_perm [R, d] at ((i / 32) * R + r) * 32 + i % 32, so one
+// 32-wide K block of consecutive rows is one contiguous run.  Thread unit u =
+// (block, row, 16-byte piece) with the piece fastest: writes are contiguous.
+__global__ __launch_bounds__(256) void gather_rows_kb_kernel(const uint4* __restrict__ x,
+                                                             const int32_t* __restrict__ row_token,
+                                                             int R, int vec_per_row,
+                                                             uint4* __restrict__ x_perm) {
+    const size_t units = (size_t)R * vec_per_row;
+    for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (size_t)gridDim.x * 256) {
+        const int piece = (int)(u & 3);
+        const size_t rb = u >> 2;
+        const int r = (int)(rb % (size_t)R);
+        const int b = (int)(rb / (size_t)R);
+        const int t = row_token[r];
+        x_perm[u] = x[(size_t)t * vec_per_row + 4 * b + piece];
+    }
+}
+
 __global__ __launch_bounds__(256) void sum_splits_kernel(const float4* __restrict__ y, int splits,
                                                          size_t n4, float4* __restrict__ out) {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
@@ -140,9 +159,20 @@ hipError_t launch_route_scan(const int32_t* ids, int T, int k, int E, int32_t* c
 }
 
 hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token, int R, int d,
-                              void* x_perm, hipStream_t stream) {
+                              int kb, void* x_perm, hipStream_t stream) {
     const int esize = dtype == 0 ? 2 : 4;
     const int vec_per_row = d * esize / 16;
+    if (kb) {
+        // bf16 only: 32-element blocks are 4 16-byte pieces (d is a multiple of 64)
+        const size_t units = (size_t)R * vec_per_row;
+        size_t blocks = (units + 255) / 256;
+        if (blocks > 16384) blocks = 16384;
+        if (blocks < 1) blocks = 1;
+        hipLaunchKernelGGL(gather_rows_kb_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const uint4*>(x), row_token, R, vec_per_row,
+                           reinterpret_cast<uint4*>(x_perm));
+        return hipGetLastError();
+    }
     int blocks = (R + 3) / 4;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
