@@ -235,7 +235,7 @@ def run_stack(steps, warmup, binding, inputs, torch):
     return res
 
 
-SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384)
+SWEEP_T = (1, 2, 4, 8, 16, 32, 64, 128, 256, 384, 512, 768, 1024, 2048, 4096, 8192, 16384)
 
 
 def run_sweep(steps, warmup, binding, inputs, torch):

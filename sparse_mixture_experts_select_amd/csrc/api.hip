@@ -47,6 +47,7 @@ struct Plan {
     int variant = GEMM_LARGE_M;
     int splits = 1;
     bool g1_ksplit = false;  // streamed GEMM 1: split K over the waves of a workgroup
+    int mf = 1;              // streamed GEMMs: 16-row fragments per tile
     size_t ids = 0, gates = 0, counts = 0, offsets = 0, slot_row = 0, row_token = 0;
     size_t x_perm = 0, h = 0, y = 0, total = 0;
 };
@@ -58,17 +59,21 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
     const size_t es = dtype == MOE_DTYPE_BF16 ? 2 : 4;
     if (dtype == MOE_DTYPE_BF16) {
         const int64_t busy_experts = R < E ? R : E;
-        if (R <= 12 * E) {
-            // About a dozen rows or fewer per expert: stream the weights.
+        const bool tile_ok = R * (d > f ? d : f) * 2 < ((int64_t)1 << 31) &&
+                             d * f * 2 < ((int64_t)1 << 31);
+        if (R < 48 * E) {
+            // Under ~48 rows per expert: stream the weights, with tiles of 1,
+            // 2 or 4 row fragments of 16.
             p.variant = GEMM_STREAM;
+            p.mf = R <= 12 * E ? 1 : (R <= 24 * E ? 2 : 4);
             const int64_t nt2 = (d + 127) / 128;
-            int64_t mt = (R + 15) / 16;
+            int64_t mt = (R + 16 * p.mf - 1) / (16 * p.mf);
             if (mt < busy_experts) mt = busy_experts;
             const int64_t tiles = nt2 * mt;
             // GEMM 1 gives each wave a 128-column slab over all of K; when
             // that leaves most CUs idle (one or two tokens), split K over the
             // waves of a workgroup instead.
-            p.g1_ksplit = mt * ((f + 511) / 512) < 128;
+            p.g1_ksplit = p.mf == 1 && mt * ((f + 511) / 512) < 128;
             // GEMM 2 runs one slab per workgroup with the K range split over
             // its 4 waves; cut K further across workgroups only when that
             // leaves fewer than ~1000 waves streaming.
@@ -79,8 +84,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
             if (s > smax) s = smax;
             if (s < 1) s = 1;
             p.splits = (int)s;
-        } else if (R >= 128 * E && R * (d > f ? d : f) * 2 < ((int64_t)1 << 31) &&
-                   d * f * 2 < ((int64_t)1 << 31)) {
+        } else if (tile_ok) {
             // (the 256-row tile kernels address x_perm, h and each weight
             // matrix with 32-bit buffer offsets: each must stay under 2 GiB)
             // Many rows per expert: 256x256 macro tiles.  GEMM 2 has d/256
@@ -91,7 +95,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
             const int64_t tiles = nt2 * ((R + 255) / 256 + E / 2);
             p.splits = (tiles < 1024 && f / 64 >= 16) ? 2 : 1;
         } else {
-            // Few rows per expert: 32-row tiles; otherwise 128-row tiles.
+            // Operands past 2 GiB: 128-row tiles with 64-bit addressing.
             p.variant = (R <= 64 * E) ? GEMM_SMALL_M : GEMM_LARGE_M;
             const int64_t bm = gemm_bm(p.variant);
             const int64_t nt2 = (d + gemm2_bn(p.variant) - 1) / gemm2_bn(p.variant);
@@ -279,10 +283,11 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     LAUNCH(launch_gather_rows(dtype, x, row_token, R, di, kb, x_perm, stream), "gather_rows");
     mark(3);
     if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM) {
-        LAUNCH(launch_gemm1_swiglu_stream(x_perm, w1, w3, offsets, R, Ei, di, fi, plan.g1_ksplit, h, stream),
+        LAUNCH(launch_gemm1_swiglu_stream(x_perm, w1, w3, offsets, R, Ei, di, fi, plan.mf, plan.g1_ksplit,
+                                          h, stream),
                "gemm1_swiglu");
         mark(4);
-        LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");
+        LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.mf, plan.splits, y, stream), "gemm2");
     } else if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_TILE256) {
         LAUNCH(launch_gemm1_swiglu_tile(x_perm, w1, w3, offsets, R, Ei, di, fi, kb, h, stream), "gemm1_swiglu");
         mark(4);

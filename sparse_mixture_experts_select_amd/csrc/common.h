@@ -63,10 +63,10 @@ hipError_t launch_gemm2_f32(const void* h, const void* w2, const int32_t* offset
 // The same two contractions for batches with few rows per expert: weights are
 // streamed from HBM into registers (16-row tiles, 128-column slabs).
 hipError_t launch_gemm1_swiglu_stream(const void* x_perm, const void* w1, const void* w3,
-                                      const int32_t* offsets, int R, int E, int d, int f,
+                                      const int32_t* offsets, int R, int E, int d, int f, int mf,
                                       bool ksplit_waves, void* h, hipStream_t stream);
 hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* offsets, int R, int E,
-                               int f, int d, int splits, float* y, hipStream_t stream);
+                               int f, int d, int mf, int splits, float* y, hipStream_t stream);
 
 // The same two contractions for batches with many rows per expert: 256x256
 // macro tiles, double-buffered LDS.

@@ -5,8 +5,10 @@
 // "Method", SwiGLU pseudocode): per expert e, GEMM 1 h = SiLU(X_e.w1[e]) *
 // (X_e.w3[e]) and GEMM 2 y = h_e.w2[e], over the expert's grouped rows.
 //
-// Work unit: (expert, 16-row tile, 128-column slab(s), K slice).  Two
-// workgroup shapes, both of 4 wavefronts:
+// Work unit: (expert, tile of MF 16-row fragments, 128-column slab(s), K
+// slice); MF = 1, 2 or 4 (up to ~12, ~28, ~60 rows per expert), so each
+// weight block loaded feeds MF MFMAs.  Two workgroup shapes, both of 4
+// wavefronts:
 //   KSPLIT_WAVES: one slab; the 4 waves split the slice's K range into 4
 //                 contiguous quarters and add their partial sums in LDS once
 //                 at the end (used when there are few slabs: GEMM 2, and
@@ -54,21 +56,22 @@ __device__ __forceinline__ bf16x8 block_column(const uint4 (&v)[8], int c) {
     return __builtin_bit_cast(bf16x8, o);
 }
 
-template <bool DUAL, bool KSPLIT_WAVES>
+template <bool DUAL, bool KSPLIT_WAVES, int MF>
 __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
     void* __restrict__ C, const int32_t* __restrict__ offsets, int R, int E, int K, int N,
     int splits) {
     constexpr int NMAT = DUAL ? 2 : 1;
     constexpr int TILE_N = KSPLIT_WAVES ? kSlab : 4 * kSlab;
-    __shared__ floatx4 red[KSPLIT_WAVES ? 3 : 1][KSPLIT_WAVES ? NMAT * 8 : 1][64];
+    constexpr int TILE_M = kMT * MF;  // rows per tile: MF fragments of 16
+    __shared__ floatx4 red[KSPLIT_WAVES ? 3 : 1][KSPLIT_WAVES ? MF * NMAT * 8 : 1][64];
 
     // ---- which (expert, split, n-tile, m-tile) this workgroup computes
     const int NT = (N + TILE_N - 1) / TILE_N;
     int total = 0;
     for (int e = 0; e < E; ++e) {
         const int n_e = offsets[e + 1] - offsets[e];
-        total += ((n_e + kMT - 1) / kMT) * NT * splits;
+        total += ((n_e + TILE_M - 1) / TILE_M) * NT * splits;
     }
     const int per_xcd = (total + 7) / 8;
     const int slot = blockIdx.x >> 3;
@@ -79,14 +82,14 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
     for (e = 0; e < E; ++e) {
         const int o0 = offsets[e];
         const int n_e = offsets[e + 1] - o0;
-        const int mt = (n_e + kMT - 1) / kMT;
+        const int mt = (n_e + TILE_M - 1) / TILE_M;
         const int tiles = mt * NT * splits;
         if (L < tiles) {
             const int m = L % mt;
             const int rest = L / mt;
             n_tile = rest % NT;
             split = rest / NT;
-            row0 = o0 + m * kMT;
+            row0 = o0 + m * TILE_M;
             row_end = o0 + n_e;
             break;
         }
@@ -110,8 +113,12 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
         k1 = min(k0 + q, s1);
     }
 
-    const int arow = min(row0 + j, row_end - 1);
-    const bf16* a_ptr = A + (size_t)arow * K + 8 * g;
+    // A fragment f: rows row0 + 16 f + j (past the expert: its last row, a
+    // valid address feeding only rows that are never stored).
+    const bf16* a_ptr[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f)
+        a_ptr[f] = A + (size_t)min(row0 + 16 * f + j, row_end - 1) * K + 8 * g;
     const int col = n_tile * TILE_N + (KSPLIT_WAVES ? 0 : wave * kSlab) + 8 * j;
     const bool b_ok = col < N;
     const size_t b_off = (size_t)e * K * N + (size_t)(8 * g) * N + (b_ok ? col : 0);
@@ -119,14 +126,18 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
     b_ptr[0] = B0 + b_off;
     if (DUAL) b_ptr[NMAT - 1] = B1 + b_off;
 
-    floatx4 acc[NMAT][8];
+    floatx4 acc[MF][NMAT][8];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int f = 0; f < MF; ++f)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[m][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[f][m][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     for (int kt = k0; kt < k1; ++kt) {
-        const uint4 a = *reinterpret_cast<const uint4*>(a_ptr + (size_t)kt * kKS);
+        uint4 a[MF];
+#pragma unroll
+        for (int f = 0; f < MF; ++f) a[f] = *reinterpret_cast<const uint4*>(a_ptr[f] + (size_t)kt * kKS);
         uint4 v[NMAT][8];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
@@ -134,68 +145,79 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 8; ++r) v[m][r] = *reinterpret_cast<const uint4*>(p + (size_t)r * N);
         }
-        const bf16x8 af = __builtin_bit_cast(bf16x8, a);
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, block_column(v[m], c),
-                                                                    acc[m][c], 0, 0, 0);
+            for (int c = 0; c < 8; ++c) {
+                const bf16x8 bf = block_column(v[m], c);
+#pragma unroll
+                for (int f = 0; f < MF; ++f)
+                    acc[f][m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, a[f]), bf, acc[f][m][c], 0, 0, 0);
+            }
     }
 
     if (KSPLIT_WAVES) {
         // ---- add the four quarters
         if (wave > 0) {
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
+            for (int f = 0; f < MF; ++f)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) red[wave - 1][m * 8 + c][lane] = acc[m][c];
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+                        red[wave - 1][(f * NMAT + m) * 8 + c][lane] = acc[f][m][c];
         }
         __syncthreads();
         if (wave != 0) return;
 #pragma unroll
         for (int w = 0; w < 3; ++w)
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m)
+            for (int f = 0; f < MF; ++f)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[m][c] += red[w][m * 8 + c][lane];
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[f][m][c] += red[w][(f * NMAT + m) * 8 + c][lane];
     }
 
     if (!b_ok) return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = row0 + 4 * g + i;
-        if (row >= row_end) continue;
-        if (DUAL) {
-            uint32_t w[4];
+    for (int f = 0; f < MF; ++f)
 #pragma unroll
-            for (int c2 = 0; c2 < 4; ++c2) {
-                const float h0 = silu_f32(acc[0][2 * c2][i]) * acc[1][2 * c2][i];
-                const float h1 = silu_f32(acc[0][2 * c2 + 1][i]) * acc[1][2 * c2 + 1][i];
-                w[c2] = pack_bf16x2(h0, h1);
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 16 * f + 4 * g + i;
+            if (row >= row_end) continue;
+            if (DUAL) {
+                uint32_t w[4];
+#pragma unroll
+                for (int c2 = 0; c2 < 4; ++c2) {
+                    const float h0 = silu_f32(acc[f][0][2 * c2][i]) * acc[f][1][2 * c2][i];
+                    const float h1 = silu_f32(acc[f][0][2 * c2 + 1][i]) * acc[f][1][2 * c2 + 1][i];
+                    w[c2] = pack_bf16x2(h0, h1);
+                }
+                *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(C) + (size_t)row * N + col) =
+                    make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+                float* y = reinterpret_cast<float*>(C) + (size_t)split * R * N + (size_t)row * N + col;
+                reinterpret_cast<float4*>(y)[0] =
+                    make_float4(acc[f][0][0][i], acc[f][0][1][i], acc[f][0][2][i], acc[f][0][3][i]);
+                reinterpret_cast<float4*>(y)[1] =
+                    make_float4(acc[f][0][4][i], acc[f][0][5][i], acc[f][0][6][i], acc[f][0][7][i]);
             }
-            *reinterpret_cast<uint4*>(reinterpret_cast<bf16*>(C) + (size_t)row * N + col) =
-                make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-            float* y = reinterpret_cast<float*>(C) + (size_t)split * R * N + (size_t)row * N + col;
-            reinterpret_cast<float4*>(y)[0] =
-                make_float4(acc[0][0][i], acc[0][1][i], acc[0][2][i], acc[0][3][i]);
-            reinterpret_cast<float4*>(y)[1] =
-                make_float4(acc[0][4][i], acc[0][5][i], acc[0][6][i], acc[0][7][i]);
         }
-    }
 }
 
-template <bool DUAL, bool KSPLIT_WAVES>
+template <bool DUAL, bool KSPLIT_WAVES, int MF>
 hipError_t launch_stream(const void* A, const void* B0, const void* B1, void* C,
                          const int32_t* offsets, int R, int E, int K, int N, int splits,
                          hipStream_t stream) {
     const long long tile_n = KSPLIT_WAVES ? kSlab : 4 * kSlab;
     const long long NT = (N + tile_n - 1) / tile_n;
-    const long long mtiles = (R + kMT - 1) / kMT + E;  // bound on sum_e ceil(n_e / 16)
+    const long long tile_m = kMT * MF;
+    const long long mtiles = (R + tile_m - 1) / tile_m + E;  // bound on sum_e ceil(n_e / tile_m)
     long long grid = mtiles * NT * splits;
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((stream_gemm_kernel<DUAL, KSPLIT_WAVES>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((stream_gemm_kernel<DUAL, KSPLIT_WAVES, MF>), dim3((unsigned)grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const bf16*>(A),
                        reinterpret_cast<const bf16*>(B0), reinterpret_cast<const bf16*>(B1), C,
                        offsets, R, E, K, N, splits);
@@ -205,16 +227,20 @@ hipError_t launch_stream(const void* A, const void* B0, const void* B1, void* C,
 }  // namespace
 
 hipError_t launch_gemm1_swiglu_stream(const void* x_perm, const void* w1, const void* w3,
-                                      const int32_t* offsets, int R, int E, int d, int f,
+                                      const int32_t* offsets, int R, int E, int d, int f, int mf,
                                       bool ksplit_waves, void* h, hipStream_t stream) {
     if (ksplit_waves)
-        return launch_stream<true, true>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
-    return launch_stream<true, false>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
+        return launch_stream<true, true, 1>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
+    if (mf >= 4) return launch_stream<true, false, 4>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
+    if (mf == 2) return launch_stream<true, false, 2>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
+    return launch_stream<true, false, 1>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
 }
 
 hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* offsets, int R, int E,
-                               int f, int d, int splits, float* y, hipStream_t stream) {
-    return launch_stream<false, true>(h, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+                               int f, int d, int mf, int splits, float* y, hipStream_t stream) {
+    if (mf >= 4) return launch_stream<false, true, 4>(h, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+    if (mf == 2) return launch_stream<false, true, 2>(h, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+    return launch_stream<false, true, 1>(h, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
 }
 
 }  // namespace moe

@@ -56,6 +56,8 @@ SMALL = [
     (20, 256, 1024, 8, 2, torch.bfloat16),    # K split 8, one step per wave
     (5, 128, 128, 64, 8, torch.bfloat16),     # E = 64, most experts empty
     (2, 256, 1024, 8, 2, torch.bfloat16),     # GEMM 1 with K split over the waves
+    (110, 192, 320, 8, 2, torch.bfloat16),    # streamed, 2 row fragments per tile, ragged slabs
+    (200, 256, 512, 8, 2, torch.bfloat16),    # streamed, 4 row fragments per tile
     (50, 100, 60, 5, 2, torch.float32),
     (200, 64, 96, 16, 4, torch.float32),
 ]
@@ -76,6 +78,16 @@ def test_small_shapes(T, d, f, E, k, dtype):
     torch.cuda.synchronize()
     assert torch.equal(plain.view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
                        r["gpu"]["out"].view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+
+
+def test_batch_with_h_past_2gib():
+    """h = 65600 x 16384 bf16 is past 2 GiB: the GEMMs fall back from the
+    256-row tile kernels (32-bit buffer offsets) to the 128-row grouped ones."""
+    banner("T=32800 d=128 f=16384 E=8 k=2 (h > 2 GiB)")
+    inp = case(32800, 128, 16384, 8, torch.bfloat16, seed=12, label="huge")
+    r = PT.full_check(inp, 2, tokens=np.arange(0, 32800, 2050), want_h=False, want_y=False,
+                      label="huge")
+    print("near ties", r["near_ties"], "err", r["err_out"])
 
 
 def test_all_logits_tied():
