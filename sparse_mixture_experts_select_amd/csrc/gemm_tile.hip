@@ -12,14 +12,23 @@
 // accumulators (8 x 8 fragments of v_mfma_f32_16x16x32_bf16, 256 fp32 per
 // lane, held in AGPRs), so every fragment read from LDS feeds 8 MFMAs.
 //
+// Tail tiles.  An expert's rows past its last multiple of 256, when there are
+// at most 128 of them, form a tail tile of 128 rows x two column tiles: the
+// two row halves of the waves (wm) take one column tile each, all waves read
+// the same 128 A rows.  Such a tile loads 8 KiB of A and 32 KiB of B per K
+// step (40 KiB against 32 KiB for a full tile) and covers two column tiles,
+// where a 256-row tile would spend a full tile's loads and MFMAs per column
+// tile on rows that do not exist.  The kernel is data-movement bound, so a
+// tail tile costs about 1.25 full tiles for the work of two.
+//
 // Staging: global -> LDS by DMA (buffer_load_dwordx4 ... lds: lane l's 16
 // bytes land at the wave's LDS base + 16 l).  SGPR buffer descriptors over A
 // and the expert's weights; each lane's byte offset is fixed for the whole
 // loop and a wave-uniform offset advances per K step.  Four LDS stages of
-// 32 KiB, loads three K steps ahead.  The one barrier of a step sits half
+// 40 KiB (a full tile uses 32 KiB of each), loads three K steps ahead.  The one barrier of a step sits half
 // way through its MFMAs: before it each wave waits for its own loads of the
-// next stage (always exactly vmcnt(8): past the end the refills repeat the
-// last step, valid addresses never read); after it the wave refills the
+// next stage (always exactly vmcnt(8), vmcnt(10) in a tail tile: past the
+// end the refills repeat the last step, valid addresses never read); after it the wave refills the
 // stage of the previous step and reads the next step's A fragments under the
 // second half of the MFMAs, so a step starts with its operands in registers.
 // No register holds staged data and no VALU work is spent on it.  The
@@ -44,9 +53,11 @@
 // The DMA lane order fixes the LDS address, so each lane simply loads the
 // global chunk that belongs at its swizzled LDS position.
 //
-// Order.  Tiles are numbered (expert, K slice, n-tile, m-tile), m fastest, and
-// each XCD takes a contiguous run of them (workgroup IDs are dealt to the 8
-// XCDs round-robin), so workgroups that share a weight panel run together and
+// Order.  Tiles are numbered by expert, then K slice, then pairs of column
+// tiles; within a pair, the full-row tiles of the first column tile (m
+// fastest), those of the second, then the pair's tail tile.  Each XCD takes a
+// contiguous run of tile numbers (workgroup IDs are dealt to the 8 XCDs
+// round-robin), so workgroups that share a weight panel run together and
 // share one L2.
 //
 // Epilogue.  GEMM 1 forms SiLU(a) * b, stages the bf16 tile in LDS (two of the
@@ -61,15 +72,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBM = 256;
 constexpr int kBK = 32;
-constexpr int kCols = 256;                             // weight columns staged per step
-constexpr int kAUnits = kBM * kBK / 8;                 // 1024 16-byte units
-constexpr int kBUnits = kBK * kCols / 8;               // 1024 16-byte units
-constexpr int kStageBytes = (kAUnits + kBUnits) * 16;  // 32 KiB
-constexpr int kBOffset = kAUnits * 16;                 // B part of a stage
-constexpr int kBHalfBytes = kBK * 128 * 2;             // one 128-column half of B
+constexpr int kStageBytes = 40 * 1024;  // full tile: A 16 KiB + B 16 KiB; tail tile: A 8 + B 32
+constexpr int kBOffFull = 16 * 1024;    // B part of a stage, full tile
+constexpr int kBOffTail = 8 * 1024;     // B part of a stage, tail tile
+constexpr int kBHalfBytes = kBK * 128 * 2;  // one 128-column block of B (8 KiB)
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4_t lds_short4;
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
     void* __restrict__ C, const int32_t* __restrict__ offsets, int R, int E, int K, int N,
     int splits, int kb) {
-    constexpr int BN = DUAL ? 128 : 256;  // output columns per tile
+    constexpr int BN = DUAL ? 128 : 256;  // output columns per column tile
     // One array per stage: the compiler can then tell the stage being read
     // from the stages the DMA is writing, and does not wait for those loads.
     __shared__ __align__(16) unsigned char st0[kStageBytes];
@@ -103,34 +111,53 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     __shared__ __align__(16) unsigned char st2[kStageBytes];
     __shared__ __align__(16) unsigned char st3[kStageBytes];
 
-    // ---- tile lookup
+    // ---- tile lookup.  Per expert with n_e rows: mt_n row tiles of 256 (the
+    // last one partial when more than 128 rows remain) per column tile, plus
+    // one tail tile per pair of column tiles when 1..128 rows remain.
     const int NT = (N + BN - 1) / BN;
+    const int NTP = (NT + 1) / 2;
     int total = 0;
     for (int e = 0; e < E; ++e) {
         const int n_e = offsets[e + 1] - offsets[e];
-        total += ((n_e + kBM - 1) / kBM) * NT * splits;
+        const int rem = n_e & (kBM - 1);
+        const int mt_n = (n_e >> 8) + (rem > 128 ? 1 : 0);
+        const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
+        total += (mt_n * NT + tail * NTP) * splits;
     }
     const int per_xcd = (total + 7) / 8;
     const int slot = blockIdx.x >> 3;
     if (slot >= per_xcd) return;
     int L = (blockIdx.x & 7) * per_xcd + slot;
     if (L >= total) return;
-    int e = 0, row0 = 0, row_end = 0, n_tile = 0, split = 0;
+    int e = 0, row0 = 0, row_end = 0, col0 = 0, split = 0;
+    bool is_tail = false;
     for (e = 0; e < E; ++e) {
         const int o0 = offsets[e];
         const int n_e = offsets[e + 1] - o0;
-        const int mt = (n_e + kBM - 1) / kBM;
-        const int tiles = mt * NT * splits;
-        if (L < tiles) {
-            const int m = L % mt;
-            const int rest = L / mt;
-            n_tile = rest % NT;
-            split = rest / NT;
-            row0 = o0 + m * kBM;
+        const int rem = n_e & (kBM - 1);
+        const int mt_n = (n_e >> 8) + (rem > 128 ? 1 : 0);
+        const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
+        const int per_split = mt_n * NT + tail * NTP;
+        if (L < per_split * splits) {
+            split = L / per_split;
+            const int Lr = L - split * per_split;
+            const int bs = 2 * mt_n + tail;  // tiles per pair of column tiles (the last
+                                             // pair has one column tile when NT is odd)
+            const int q = min(Lr / bs, NTP - 1);
+            const int r = Lr - q * bs;
+            const int n_in = (2 * q + 1 < NT) ? 2 : 1;
+            if (r < mt_n * n_in) {
+                col0 = (2 * q + r / mt_n) * BN;
+                row0 = o0 + (r % mt_n) * kBM;
+            } else {
+                is_tail = true;
+                col0 = 2 * q * BN;
+                row0 = o0 + (n_e >> 8) * kBM;
+            }
             row_end = o0 + n_e;
             break;
         }
-        L -= tiles;
+        L -= per_split * splits;
     }
 
     const int tid = threadIdx.x;
@@ -138,7 +165,8 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     const int wave = tid >> 6;
     const int wm = wave >> 1;
     const int wn = wave & 1;
-    const int col0 = n_tile * BN;
+    const int lrow = lane & 15;
+    const int lgrp = lane >> 4;
 
     const int KT = K / kBK;
     const int kt_per = (KT + splits - 1) / splits;
@@ -147,9 +175,10 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 
     // ---- DMA sources.  Buffer descriptors (SGPRs) over A and over the
     // expert's weight matrices; per lane a loop-invariant byte offset, per K
-    // step a wave-uniform one.  Unit u = 256 i + 64 wave + lane (i = 0..3) of
-    // each stage part; the wave's LDS destination for instruction i is
-    // part base + (256 i + 64 wave) * 16.
+    // step a wave-uniform one.  Unit u = 256 i + 64 wave + lane of each stage
+    // part; the wave's LDS destination for instruction i is part base +
+    // (256 i + 64 wave) * 16.  A: 4 instructions (256 rows; 2 in a tail tile),
+    // B: 4 (two 128-column blocks; 8 and four blocks in a tail tile).
     const __amdgpu_buffer_rsrc_t a_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0x7fffffff, 0x00020000);
     const bf16* bh0 = B0 + (size_t)e * K * N;
@@ -159,11 +188,10 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     const __amdgpu_buffer_rsrc_t b_rsrc1 =
         __builtin_amdgcn_make_buffer_rsrc((void*)bh1, (short)0, 0x7fffffff, 0x00020000);
     int a_voff[4];
-    int b_voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int u = 256 * i + 64 * wave + lane;
-        // A: row r = u/4; stored chunk u%4 holds logical chunk (u%4) ^ ((r/2)%4).
+        // row r = u/4; stored chunk u%4 holds logical chunk (u%4) ^ ((r/2)%4).
         const int r = u >> 2;
         const int c = (u & 3) ^ ((r >> 1) & 3);
         const int grow = min(row0 + r, row_end - 1);  // rows past the expert only feed unstored rows
@@ -171,42 +199,50 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         // row grow at grow * 32 within it (one K step of 256 rows is 16 KiB
         // of contiguous memory, read in full 128-byte lines)
         a_voff[i] = (kb ? grow * 32 + 8 * c : grow * K + 8 * c) * 2;
-        // B: half h = u/512 (instructions 0,1 -> half 0, 2,3 -> half 1); within
-        // the half, k row kk = (u%512)/16 and stored unit p = u%16 is group
-        // (p/2) ^ swz(kk), 8-column piece p%2.
+    }
+    // B block h of the stage (h = i/2): GEMM 1 full tile: w1 | w3 of the
+    // column tile; tail: w1 | w3 of the first column tile, then of the second.
+    // GEMM 2: 128-column blocks left to right (one column tile per two
+    // blocks).  Within a block, k row kk = (u%512)/16 and stored unit p = u%16
+    // is group (p/2) ^ swz(kk), 8-column piece p%2.
+    int b_voff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int u = 256 * i + 64 * wave + lane;
         const int v = u & 511;
         const int kk = v >> 4;
         const int p = v & 15;
         const int col = 16 * ((p >> 1) ^ b_group_swz(kk)) + 8 * (p & 1);
-        int gcol = (DUAL ? col0 : col0 + 128 * (i >> 1)) + col;
+        const int h = i >> 1;
+        int gcol = (DUAL ? col0 + BN * (h >> 1) : col0 + 128 * h) + col;
         if (gcol >= N) gcol = 0;  // columns past N only feed unstored columns
         b_voff[i] = (kk * N + gcol) * 2;
     }
     const int a_step = kb ? R * kBK * 2 : kBK * 2;  // bytes per K step in A
-    const int b_step = kBK * N * 2;  // bytes per K step in B
+    const int b_step = kBK * N * 2;                 // bytes per K step in B
 
     // ---- fragment addressing (bytes within a stage)
-    const int lrow = lane & 15;
-    const int lgrp = lane >> 4;
-    // A fragment m: row wm*128 + 16 m + lrow, chunk lgrp, stored at chunk
-    // lgrp ^ ((row/2)%4) = lgrp ^ ((lrow/2)%4) for every m.
-    const int a_frag = (wm * 128 + lrow) * 64 + 16 * (lgrp ^ ((lrow >> 1) & 3));
-    // B fragment n: 16 columns of one half; lane (lgrp, lrow) addresses k row
+    // A fragment m: row 16 m + lrow of this wave's 128 rows (rows wm*128.. in a
+    // full tile, the tail's 128 rows for every wave), chunk lgrp, stored at
+    // chunk lgrp ^ ((row/2)%4) = lgrp ^ ((lrow/2)%4).
+    const int a_frag = ((is_tail ? 0 : wm * 128) + lrow) * 64 + 16 * (lgrp ^ ((lrow >> 1) & 3));
+    // B fragment n: 16 columns of one block; lane (lgrp, lrow) addresses k row
     // 8 lgrp + lrow/4 (+4 for the second read), columns 4 (lrow%4) .. +3.
     const int b_k = 8 * lgrp + (lrow >> 2);
     const int b_swz = b_group_swz(b_k);  // the same for b_k + 4
     int b_frag[8];
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-        int half, g;
+        int blk, g;
         if (DUAL) {
-            half = n >> 2;
+            blk = (is_tail ? 2 * wm : 0) + (n >> 2);
             g = 4 * wn + (n & 3);
         } else {
-            half = wn;
+            blk = (is_tail ? 2 * wm : 0) + wn;
             g = n;
         }
-        b_frag[n] = kBOffset + half * kBHalfBytes + b_k * 256 + 32 * (g ^ b_swz) + 8 * (lrow & 3);
+        b_frag[n] = (is_tail ? kBOffTail : kBOffFull) + blk * kBHalfBytes + b_k * 256 +
+                    32 * (g ^ b_swz) + 8 * (lrow & 3);
     }
 
     floatx4 acc[8][8];
@@ -215,23 +251,24 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 #pragma unroll
         for (int n = 0; n < 8; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-#define MOE_ISSUE_STAGE(KT_, ARR_)                                                          \
+    // Loads of one K step: NA_ A and NB_ B instructions per lane.
+#define MOE_ISSUE_STAGE(KT_, ARR_, NA_, NB_, BOFF_)                                         \
     do {                                                                                    \
         lds_char* sb_ = (lds_char*)(lds_void*)(ARR_) + (64 * wave) * 16;                    \
         const int ka_ = (KT_) * a_step;                                                     \
         const int kb_ = (KT_) * b_step;                                                     \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                    \
+        _Pragma("unroll") for (int i_ = 0; i_ < (NA_); ++i_)                                \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void*)(sb_ + 4096 * i_), \
                                                      16, a_voff[i_], ka_, 0, 0);            \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                    \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(i_ < 2 ? b_rsrc0 : b_rsrc1,           \
-                                                     (lds_void*)(sb_ + kBOffset + 4096 * i_), \
-                                                     16, b_voff[i_], kb_, 0, 0);            \
+        _Pragma("unroll") for (int i_ = 0; i_ < (NB_); ++i_)                                \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                       \
+                (DUAL ? ((i_ >> 1) & 1) : 0) ? b_rsrc1 : b_rsrc0,                            \
+                (lds_void*)(sb_ + (BOFF_) + 4096 * i_), 16, b_voff[i_], kb_, 0, 0);         \
     } while (0)
 
-#define MOE_READ_A(ST_, M_)                                                                 \
+#define MOE_READ_A(ARR_, M_)                                                                \
     (*reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(                    \
-        (const lds_char*)(lds_void*)(ST_) + a_frag + (M_) * 16 * 64))
+        (const lds_char*)(lds_void*)(ARR_) + a_frag + (M_) * 16 * 64))
 
 #define MOE_READ_B(ST_, N_)                                                                 \
     __builtin_bit_cast(bf16x8, __builtin_shufflevector(                                     \
@@ -245,20 +282,20 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 
 // Scheduling hints: within a group of 8 MFMAs, put one of the group's LDS
 // reads (for fragments two groups ahead) after each of the first NR_ MFMAs,
-// and NV_ of the stage refill's DMA loads after MFMAs 3 and 6, so the wave
+// and NV_ of the stage refill's DMA loads among the later MFMAs, so the wave
 // never holds a burst of memory instructions while the matrix core idles.
 #define MOE_SCHED_GROUP(NR_, NV_)                                                           \
     _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                      \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
         if (i_ < (NR_)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  \
-        if ((i_ == 2 && (NV_) > 0) || (i_ == 5 && (NV_) > 1))                               \
+        if ((i_ == 2 && (NV_) > 0) || (i_ == 5 && (NV_) > 1) || (i_ == 7 && (NV_) > 2))     \
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                              \
     }
 
     // One K step on stage CUR_.  On entry af[] holds its A fragments and
     // bq0, bq1 its first two B fragments; B fragment n + 2 is read while the
     // MFMAs of fragment n run.  Half way (before fragment 4): wait until this
-    // wave's loads of the next stage NXT_ are complete (vmcnt(8): only the
+    // wave's loads of the next stage NXT_ are complete (vmcnt(NV_): only the
     // stage after it may still be in flight), barrier (now every wave's loads
     // of NXT_ have landed, and every wave has consumed its reads of REF_, the
     // stage of the previous step), refill REF_ with step kt + 3, and read the
@@ -269,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     // and issues its (repeated, never read) refill, so every path through the
     // loop issues the same sequence of DMA loads: the compiler's DMA wait
     // tracking then stays per stage across the guards' control-flow merges.
-#define MOE_STEP(CUR_, NXT_, REF_)                                                          \
+#define MOE_STEP(CUR_, NXT_, REF_, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                     \
     {                                                                                       \
         const lds_char* st_ = (const lds_char*)(lds_void*)(CUR_);                           \
         const bool live_ = kt < kt1;                                                        \
@@ -288,9 +325,9 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
             MOE_SCHED_GROUP(2, 0);                                                          \
             MOE_SCHED_GROUP(2, 0);                                                          \
         }                                                                                   \
-        MOE_WAIT_VM(8);                                                                     \
+        MOE_WAIT_VM((NA_) + (NB_));                                                         \
         stage_barrier();                                                                    \
-        MOE_ISSUE_STAGE(min(kt + 3, kt1 - 1), REF_);                                        \
+        MOE_ISSUE_STAGE(min(kt + 3, kt1 - 1), REF_, NA_, NB_, BOFF_);                       \
         if (live_) {                                                                        \
             const lds_char* sn_ = (const lds_char*)(lds_void*)(NXT_);                       \
             bf16x8 an[8];                                                                   \
@@ -310,40 +347,47 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
             MOE_MFMAS(6, b6_);                                                              \
             bq1 = MOE_READ_B(sn_, 1);                                                       \
             MOE_MFMAS(7, b7_);                                                              \
-            MOE_SCHED_GROUP(4, 2);                                                          \
-            MOE_SCHED_GROUP(4, 2);                                                          \
-            MOE_SCHED_GROUP(6, 2);                                                          \
-            MOE_SCHED_GROUP(2, 2);                                                          \
+            MOE_SCHED_GROUP(4, G4_);                                                        \
+            MOE_SCHED_GROUP(4, G5_);                                                        \
+            MOE_SCHED_GROUP(6, G6_);                                                        \
+            MOE_SCHED_GROUP(2, G7_);                                                        \
             _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_) af[m_] = an[m_];               \
         }                                                                                   \
         ++kt;                                                                               \
     }
 
-    // Loads in flight: the prologue fills st0, st1, st2 with steps kt0,
-    // kt0+1, kt0+2 and waits for the first; each step refills one stage half
-    // way through, so at every half-way wait exactly two younger steps are in
-    // flight and one fixed vmcnt(8) leaves the next step's loads complete.
-    // Past the last step the refills repeat it (valid addresses, never read).
+    // The K loop for one tile shape.  Loads in flight: the prologue fills
+    // st0, st1, st2 with steps kt0, kt0+1, kt0+2 and waits for the first;
+    // each step refills one stage half way through, so at every half-way wait
+    // exactly two younger steps are in flight and one fixed vmcnt leaves the
+    // next step's loads complete.  Past the last step the refills repeat it
+    // (valid addresses, never read).
+#define MOE_K_LOOP(NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                                     \
+    {                                                                                       \
+        MOE_ISSUE_STAGE(kt0, st0, NA_, NB_, BOFF_);                                         \
+        MOE_ISSUE_STAGE(min(kt0 + 1, kt1 - 1), st1, NA_, NB_, BOFF_);                       \
+        MOE_ISSUE_STAGE(min(kt0 + 2, kt1 - 1), st2, NA_, NB_, BOFF_);                       \
+        MOE_WAIT_VM(2 * ((NA_) + (NB_)));                                                   \
+        stage_barrier();                                                                    \
+        bf16x8 af[8];                                                                       \
+        _Pragma("unroll") for (int m = 0; m < 8; ++m) af[m] = MOE_READ_A(st0, m);           \
+        const lds_char* s0_ = (const lds_char*)(lds_void*)st0;                              \
+        bf16x8 bq0 = MOE_READ_B(s0_, 0);                                                    \
+        bf16x8 bq1 = MOE_READ_B(s0_, 1);                                                    \
+        while (kt < kt1) {                                                                  \
+            MOE_STEP(st0, st1, st3, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                    \
+            MOE_STEP(st1, st2, st0, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                    \
+            MOE_STEP(st2, st3, st1, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                    \
+            MOE_STEP(st3, st0, st2, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                    \
+        }                                                                                   \
+    }
+
     int kt = kt0;
     if (kt0 < kt1) {
-        MOE_ISSUE_STAGE(kt0, st0);
-        MOE_ISSUE_STAGE(min(kt0 + 1, kt1 - 1), st1);
-        MOE_ISSUE_STAGE(min(kt0 + 2, kt1 - 1), st2);
-        MOE_WAIT_VM(16);
-        stage_barrier();
-        bf16x8 af[8];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) af[m] = MOE_READ_A(st0, m);
-        const lds_char* s0_ = (const lds_char*)(lds_void*)st0;
-        bf16x8 bq0 = MOE_READ_B(s0_, 0);
-        bf16x8 bq1 = MOE_READ_B(s0_, 1);
-        while (kt < kt1) {
-            MOE_STEP(st0, st1, st3)
-            MOE_STEP(st1, st2, st0)
-            MOE_STEP(st2, st3, st1)
-            MOE_STEP(st3, st0, st2)
-        }
+        if (is_tail) MOE_K_LOOP(2, 8, kBOffTail, 3, 3, 2, 2)
+        else MOE_K_LOOP(4, 4, kBOffFull, 2, 2, 2, 2)
     }
+#undef MOE_K_LOOP
 #undef MOE_SCHED_GROUP
 #undef MOE_MFMAS
 #undef MOE_READ_B
@@ -356,8 +400,9 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     // ---- epilogue: lane holds rows 4*lgrp + r (r = 0..3) of column lrow of each fragment.
     if (DUAL) {
         __syncthreads();  // every wave is done reading the stages
-        // Stage the 256 x 128 bf16 tile of h in LDS: rows 0..127 (wm = 0) in
-        // st0, rows 128..255 in st1, 256 bytes per row, 16-byte chunk ch of
+        // Stage the wave pair's 128 x 128 bf16 block of h in LDS (wm = 0 in
+        // st0, wm = 1 in st1; full tile: rows 0..127 | 128..255, tail tile:
+        // first | second column tile), 256 bytes per row, 16-byte chunk ch of
         // row r stored at ch ^ (r % 16).
         uint16_t* hs_w = reinterpret_cast<uint16_t*>(wm == 0 ? st0 : st1);
 #pragma unroll
@@ -366,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
             for (int n = 0; n < 4; ++n)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * m + 4 * lgrp + r;  // within this wave's 128 rows
+                    const int row = 16 * m + 4 * lgrp + r;  // within the block's 128 rows
                     const int c = wn * 64 + 16 * n + lrow;
                     const float hv = silu_f32(acc[m][n][r]) * acc[m][n + 4][r];
                     hs_w[row * 128 + (((c >> 3) ^ (row & 15)) << 3) + (c & 7)] =
@@ -374,20 +419,21 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
                 }
         __syncthreads();
         uint16_t* h = reinterpret_cast<uint16_t*>(C);
+        // staged row sr = 0..255: block sr/128, row sr%128 of that block
         if (kb) {
-            // K-blocked h: for each of the tile's 4 blocks of 32 columns, its
-            // 256 rows are one contiguous run of 64-byte row pieces.
+            // K-blocked h: for each block of 32 columns, consecutive rows are
+            // one contiguous run of 64-byte row pieces.
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int idx = tid + kThreads * q;
                 const int piece = idx & 3;        // 16-byte piece of the 64-byte row segment
-                const int row = (idx >> 2) & 255;
-                const int b = idx >> 10;          // block of 32 columns within the tile
+                const int sr = (idx >> 2) & 255;
+                const int b = idx >> 10;          // block of 32 columns within the 128
                 const int ch = 4 * b + piece;     // 16-byte chunk of the staged row
-                const int grow = row0 + row;
-                const int gc = col0 + ch * 8;
-                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(row < 128 ? st0 : st1);
-                const int rr = row & 127;
+                const int rr = sr & 127;
+                const int grow = row0 + (is_tail ? rr : sr);
+                const int gc = col0 + (is_tail ? (sr >> 7) * BN : 0) + ch * 8;
+                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(sr < 128 ? st0 : st1);
                 if (grow < row_end && gc < N)
                     *reinterpret_cast<uint4*>(h + ((size_t)(gc >> 5) * R + grow) * 32 + (gc & 31)) =
                         *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
@@ -396,12 +442,12 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int idx = tid + kThreads * q;
-                const int row = idx >> 4;   // 0..255
+                const int sr = idx >> 4;    // 0..255
                 const int ch = idx & 15;    // 16-byte chunk of the row
-                const int grow = row0 + row;
-                const int gc = col0 + ch * 8;
-                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(row < 128 ? st0 : st1);
-                const int rr = row & 127;
+                const int rr = sr & 127;
+                const int grow = row0 + (is_tail ? rr : sr);
+                const int gc = col0 + (is_tail ? (sr >> 7) * BN : 0) + ch * 8;
+                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(sr < 128 ? st0 : st1);
                 if (grow < row_end && gc < N)
                     *reinterpret_cast<uint4*>(h + (size_t)grow * N + gc) =
                         *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
@@ -409,15 +455,17 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         }
     } else {
         float* y = reinterpret_cast<float*>(C) + (size_t)split * R * N;
+        const int rbase = row0 + (is_tail ? 0 : wm * 128);
+        const int cbase = col0 + (is_tail ? wm * BN : 0) + wn * 128;
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int grow = row0 + wm * 128 + 16 * m + 4 * lgrp + r;
+                const int grow = rbase + 16 * m + 4 * lgrp + r;
                 if (grow >= row_end) continue;
 #pragma unroll
                 for (int n = 0; n < 8; ++n) {
-                    const int gc = col0 + wn * 128 + 16 * n + lrow;
+                    const int gc = cbase + 16 * n + lrow;
                     if (gc < N) y[(size_t)grow * N + gc] = acc[m][n][r];
                 }
             }
@@ -430,7 +478,9 @@ hipError_t launch_tile(const void* A, const void* B0, const void* B1, void* C,
                        hipStream_t stream) {
     const long long BN = DUAL ? 128 : 256;
     const long long NT = (N + BN - 1) / BN;
-    const long long mtiles = (R + kBM - 1) / kBM + E;  // bound on sum_e ceil(n_e / 256)
+    // bound on the tile count: per expert at most ceil(n_e / 256) row tiles
+    // per column tile (a tail tile covers two column tiles)
+    const long long mtiles = (R + kBM - 1) / kBM + E;
     long long grid = mtiles * NT * splits;
     grid = (grid + 7) / 8 * 8;
     hipLaunchKernelGGL((tile_gemm_kernel<DUAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
