@@ -7,7 +7,9 @@
 // enqueues, in stream order:
 //   1. router_topk    x, w_router        -> ids [T,k], gates [T,k]
 //   2. route_scan     ids                -> counts, offsets, slot_row, row_token
-//   3. gather_rows    x, row_token       -> x_perm [T*k, d]
+//   3. gather_rows    x, row_token       -> x_perm [T*k, d] (the streamed
+//                                            GEMM 1 reads x through row_token
+//                                            instead, and this step is skipped)
 //   4. gemm1_swiglu   x_perm, w1, w3     -> h [T*k, f]
 //   5. gemm2          h, w2              -> y [splits][T*k, d] (fp32)
 //   6. combine        y, gates, slot_row -> out [T,d] (+ residual)
@@ -280,11 +282,13 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     // The 256-row tile GEMMs read x_perm and h in a K-blocked layout (see
     // gemm_tile.hip); a caller asking for h gets it row-major instead.
     const int kb = (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_TILE256 && !(opts && opts->h_out)) ? 1 : 0;
-    LAUNCH(launch_gather_rows(dtype, x, row_token, R, di, kb, x_perm, stream), "gather_rows");
+    // The streamed GEMM 1 reads x through row_token itself.
+    const bool gather = !(dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM);
+    if (gather) LAUNCH(launch_gather_rows(dtype, x, row_token, R, di, kb, x_perm, stream), "gather_rows");
     mark(3);
     if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM) {
-        LAUNCH(launch_gemm1_swiglu_stream(x_perm, w1, w3, offsets, R, Ei, di, fi, plan.mf, plan.g1_ksplit,
-                                          h, stream),
+        LAUNCH(launch_gemm1_swiglu_stream(x, row_token, w1, w3, offsets, R, Ei, di, fi, plan.mf,
+                                          plan.g1_ksplit, h, stream),
                "gemm1_swiglu");
         mark(4);
         LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.mf, plan.splits, y, stream), "gemm2");

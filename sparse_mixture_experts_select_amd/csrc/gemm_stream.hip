@@ -15,6 +15,8 @@
 //                 GEMM 1 when only a few experts hold rows);
 //   otherwise:    4 adjacent slabs, one per wave, each over the whole K range
 //                 (no reduction; fewer, longer-lived waves, GEMM 1).
+// GEMM 1 reads its A rows straight from the token rows of x through the
+// row -> token map (no gathered copy of x is made on this path).
 // Each wavefront streams its weight rows straight from HBM into registers:
 // per 32-row K step, lane (g = lane/16, j = lane%16) loads the 8x8 block
 // (rows 8g..8g+7 of the step, columns 8j..8j+7 of the slab) with eight
@@ -56,11 +58,13 @@ __device__ __forceinline__ bf16x8 block_column(const uint4 (&v)[8], int c) {
     return __builtin_bit_cast(bf16x8, o);
 }
 
+// a_rows: when non-null, grouped row r of A is row a_rows[r] of the A matrix
+// (GEMM 1 reading the token rows of x directly, with no gathered copy).
 template <bool DUAL, bool KSPLIT_WAVES, int MF>
 __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
-    const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
-    void* __restrict__ C, const int32_t* __restrict__ offsets, int R, int E, int K, int N,
-    int splits) {
+    const bf16* __restrict__ A, const int32_t* __restrict__ a_rows, const bf16* __restrict__ B0,
+    const bf16* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets, int R,
+    int E, int K, int N, int splits) {
     constexpr int NMAT = DUAL ? 2 : 1;
     constexpr int TILE_N = KSPLIT_WAVES ? kSlab : 4 * kSlab;
     constexpr int TILE_M = kMT * MF;  // rows per tile: MF fragments of 16
@@ -117,8 +121,10 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
     // valid address feeding only rows that are never stored).
     const bf16* a_ptr[MF];
 #pragma unroll
-    for (int f = 0; f < MF; ++f)
-        a_ptr[f] = A + (size_t)min(row0 + 16 * f + j, row_end - 1) * K + 8 * g;
+    for (int f = 0; f < MF; ++f) {
+        const int arow = min(row0 + 16 * f + j, row_end - 1);
+        a_ptr[f] = A + (size_t)(a_rows ? a_rows[arow] : arow) * K + 8 * g;
+    }
     const int col = n_tile * TILE_N + (KSPLIT_WAVES ? 0 : wave * kSlab) + 8 * j;
     const bool b_ok = col < N;
     const size_t b_off = (size_t)e * K * N + (size_t)(8 * g) * N + (b_ok ? col : 0);
@@ -208,8 +214,8 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
 }
 
 template <bool DUAL, bool KSPLIT_WAVES, int MF>
-hipError_t launch_stream(const void* A, const void* B0, const void* B1, void* C,
-                         const int32_t* offsets, int R, int E, int K, int N, int splits,
+hipError_t launch_stream(const void* A, const int32_t* a_rows, const void* B0, const void* B1,
+                         void* C, const int32_t* offsets, int R, int E, int K, int N, int splits,
                          hipStream_t stream) {
     const long long tile_n = KSPLIT_WAVES ? kSlab : 4 * kSlab;
     const long long NT = (N + tile_n - 1) / tile_n;
@@ -218,7 +224,7 @@ hipError_t launch_stream(const void* A, const void* B0, const void* B1, void* C,
     long long grid = mtiles * NT * splits;
     grid = (grid + 7) / 8 * 8;
     hipLaunchKernelGGL((stream_gemm_kernel<DUAL, KSPLIT_WAVES, MF>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, reinterpret_cast<const bf16*>(A),
+                       dim3(kThreads), 0, stream, reinterpret_cast<const bf16*>(A), a_rows,
                        reinterpret_cast<const bf16*>(B0), reinterpret_cast<const bf16*>(B1), C,
                        offsets, R, E, K, N, splits);
     return hipGetLastError();
@@ -226,21 +232,26 @@ hipError_t launch_stream(const void* A, const void* B0, const void* B1, void* C,
 
 }  // namespace
 
-hipError_t launch_gemm1_swiglu_stream(const void* x_perm, const void* w1, const void* w3,
-                                      const int32_t* offsets, int R, int E, int d, int f, int mf,
-                                      bool ksplit_waves, void* h, hipStream_t stream) {
+hipError_t launch_gemm1_swiglu_stream(const void* x, const int32_t* row_token, const void* w1,
+                                      const void* w3, const int32_t* offsets, int R, int E, int d,
+                                      int f, int mf, bool ksplit_waves, void* h,
+                                      hipStream_t stream) {
     if (ksplit_waves)
-        return launch_stream<true, true, 1>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
-    if (mf >= 4) return launch_stream<true, false, 4>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
-    if (mf == 2) return launch_stream<true, false, 2>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
-    return launch_stream<true, false, 1>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, stream);
+        return launch_stream<true, true, 1>(x, row_token, w1, w3, h, offsets, R, E, d, f, 1, stream);
+    if (mf >= 4)
+        return launch_stream<true, false, 4>(x, row_token, w1, w3, h, offsets, R, E, d, f, 1, stream);
+    if (mf == 2)
+        return launch_stream<true, false, 2>(x, row_token, w1, w3, h, offsets, R, E, d, f, 1, stream);
+    return launch_stream<true, false, 1>(x, row_token, w1, w3, h, offsets, R, E, d, f, 1, stream);
 }
 
 hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* offsets, int R, int E,
                                int f, int d, int mf, int splits, float* y, hipStream_t stream) {
-    if (mf >= 4) return launch_stream<false, true, 4>(h, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
-    if (mf == 2) return launch_stream<false, true, 2>(h, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
-    return launch_stream<false, true, 1>(h, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+    if (mf >= 4)
+        return launch_stream<false, true, 4>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+    if (mf == 2)
+        return launch_stream<false, true, 2>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+    return launch_stream<false, true, 1>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
 }
 
 }  // namespace moe

@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kBatch = 8;  // chunks of 64 ids loaded together per wave
 
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     const int32_t* __restrict__ ids, int R, int k, int E, int32_t* __restrict__ counts,
@@ -42,14 +43,23 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     const int c0 = wave * per_wave;
     const int c1 = min(c0 + per_wave, nchunks);
 
-    // Pass 1: lane e accumulates this wave's count for expert e.
+    // Pass 1: lane e accumulates this wave's count for expert e.  The ids of
+    // up to kBatch chunks are loaded together, so their latencies overlap.
     int mine = 0;
-    for (int c = c0; c < c1; ++c) {
-        const int a = c * 64 + lane;
-        const int e = a < R ? ids[a] : -1;
-        for (int ex = 0; ex < E; ++ex) {
-            const uint64_t m = __ballot(e == ex);
-            if (lane == ex) mine += __popcll(m);
+    for (int cb = c0; cb < c1; cb += kBatch) {
+        int eb[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int a = (cb + u) * 64 + lane;
+            eb[u] = (cb + u < c1 && a < R) ? ids[a] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (cb + u >= c1) break;  // wave-uniform
+            for (int ex = 0; ex < E; ++ex) {
+                const uint64_t m = __ballot(eb[u] == ex);
+                if (lane == ex) mine += __popcll(m);
+            }
         }
     }
     wave_count[wave][lane] = mine;
@@ -85,19 +95,29 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     // Pass 2: lane ex keeps the next free row of expert ex for this wave.
     int next = (lane < E) ? expert_base[lane] + wave_base[wave][lane] : 0;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int c = c0; c < c1; ++c) {
-        const int a = c * 64 + lane;
-        const int e = a < R ? ids[a] : -1;
-        int row = -1;
-        for (int ex = 0; ex < E; ++ex) {
-            const uint64_t m = __ballot(e == ex);
-            const int base = __shfl(next, ex, 64);
-            if (e == ex) row = base + __popcll(m & below);
-            if (lane == ex) next += __popcll(m);
+    for (int cb = c0; cb < c1; cb += kBatch) {
+        int eb[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int a = (cb + u) * 64 + lane;
+            eb[u] = (cb + u < c1 && a < R) ? ids[a] : -1;
         }
-        if (a < R) {
-            slot_row[a] = row;
-            row_token[row] = a / k;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (cb + u >= c1) break;  // wave-uniform
+            const int a = (cb + u) * 64 + lane;
+            const int e = eb[u];
+            int row = -1;
+            for (int ex = 0; ex < E; ++ex) {
+                const uint64_t m = __ballot(e == ex);
+                const int base = __shfl(next, ex, 64);
+                if (e == ex) row = base + __popcll(m & below);
+                if (lane == ex) next += __popcll(m);
+            }
+            if (e >= 0) {
+                slot_row[a] = row;
+                row_token[row] = a / k;
+            }
         }
     }
 }
