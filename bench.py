@@ -229,8 +229,38 @@ def run_stack(steps, warmup, binding, inputs, torch):
                   "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                   "hbm_gbs": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1)},
     }
-    log("[bench] stack: %.3f ms/step (%.4f ms/layer), %.0f tokens/s"
-        % (ms_per_step, ms_per_step / wl.layers, res["value"]))
+    # The same step replayed from one HIP graph (all 32 blocks captured;
+    # the layer calls use a caller workspace, as graph capture requires).
+    ws = torch.empty(binding.moe_ffn_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k),
+                     dtype=torch.uint8, device="cuda")
+
+    def step_ws():
+        h.copy_(h0)
+        for w in layers:
+            binding.moe_rmsnorm(h, x, eps=wl.rms_eps)
+            binding.moe_ffn_forward_ex(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=h,
+                                       residual=h, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_ws()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step_ws()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    res["graph_ms_per_step"] = round(1e3 * (time.perf_counter() - t0) / steps, 4)
+    del graph
+    log("[bench] stack: %.3f ms/step (%.4f ms/layer), %.0f tokens/s; one HIP graph: %.3f ms/step"
+        % (ms_per_step, ms_per_step / wl.layers, res["value"], res["graph_ms_per_step"]))
     del layers
     return res
 
