@@ -39,7 +39,7 @@ CSRC = os.path.join(ROOT, "sparse_mixture_experts_select_amd", "csrc")
 # kernel at a few rows per expert, the 256x256 tile kernel at >= 128 rows per
 # expert.  Patterns match both the demangled and the mangled kernel name.
 GEMM1_KERNEL = {
-    "decode": ("gemm_stream.hip", r"stream_gemm_kernel(<true, false>|ILb1ELb0E)"),
+    "decode": ("gemm_stream.hip", r"stream_gemm_kernel(<true, false|ILb1ELb0E)"),
     "prefill": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
     "skewed": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
 }
