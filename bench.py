@@ -143,8 +143,7 @@ def run_workload(name, steps, warmup, binding, inputs, torch):
         step()
     torch.cuda.synchronize()
     stage_ms, calls = binding.moe_ffn_profile_end()
-    stage_avg = {kk: v / calls for kk, v in stage_ms.items()}
-    stage_avg.pop("sum_splits", None)  # not launched by the timed calls
+    stage_avg = {kk: v / calls for kk, v in stage_ms.items() if v > 0}  # skipped stages sum to 0
 
     g_bytes, g_flops = gemm1_algorithmic(wl, counts_h)
     g_ms = timed_ms["gemm1_swiglu"] / steps
@@ -292,6 +291,13 @@ def run_sweep(steps, warmup, binding, inputs, torch):
             binding.moe_ffn_forward(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=out)
         torch.cuda.synchronize()
         ms = 1e3 * (time.perf_counter() - t0) / n
+        # per-stage breakdown from a separate pass (events at every boundary)
+        binding.moe_ffn_profile_begin(n)
+        for _ in range(n):
+            binding.moe_ffn_forward(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=out)
+        torch.cuda.synchronize()
+        st_ms, calls = binding.moe_ffn_profile_end()
+        stages = {k: round(v / max(calls, 1), 5) for k, v in st_ms.items() if v > 0}
         flops = T * (2.0 * wl.d * wl.E + wl.k * 6.0 * wl.d * wl.f)
         nbytes = active * 3 * wl.d * wl.f * 2 + wl.d * wl.E * 2 + 2 * T * wl.d * 2
         row = {"T": T, "ms": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
@@ -299,11 +305,13 @@ def run_sweep(steps, warmup, binding, inputs, torch):
                "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
                "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
-               "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+               "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "stages_ms": stages}
         rows.append(row)
         log("[sweep] T=%5d  %8.4f ms  %11.1f tokens/s  %7.1f TFLOP/s (%.3f)  %7.1f GB/s (%.3f)"
             % (T, ms, row["tokens_per_s"], row["tflops"], row["mfma_frac"], row["hbm_gbs"],
                row["hbm_frac"]))
+        log("[sweep]        stages(ms) %s" % stages)
         del x, out
     return rows
 

@@ -143,10 +143,12 @@ moe_status_t moe_rmsnorm(const void *h, void *x, int64_t T, int64_t d, float eps
  * microseconds of GPU time, so a timing run should ask only for the stages it
  * needs.  moe_ffn_profile_end waits for those events and writes the summed
  * milliseconds of each stage over the recorded calls into
- * stage_ms[MOE_NUM_STAGES] (-1 for stages not in the mask) and the number of
- * recorded calls into *calls.  Stages, in launch order: 0 router_topk,
- * 1 route_scan, 2 gather_rows, 3 gemm1_swiglu, 4 gemm2, 5 sum_splits (runs
- * only when y_out is asked for), 6 combine.  max_calls must be in [1, 1e6];
+ * stage_ms[MOE_NUM_STAGES] (-1 for stages not in the mask; a stage that a
+ * call skips, such as gather_rows on the streamed bf16 path or sum_splits
+ * without y_out, adds nothing) and the number of recorded calls into *calls.
+ * Stages, in launch order: 0 router_topk, 1 route_scan, 2 gather_rows,
+ * 3 gemm1_swiglu, 4 gemm2, 5 sum_splits (runs only when y_out is asked for),
+ * 6 combine.  max_calls must be in [1, 1e6];
  * a second begin before end, or an end without begin, is MOE_ERR_INVALID_ARG.
  * Not for concurrent use from several host threads.
  */

@@ -198,15 +198,19 @@ struct Profiler {
     int calls = 0;
     uint32_t mask = 0;         // stages timed
     hipEvent_t* ev = nullptr;  // [max_calls][MOE_NUM_STAGES + 1]
+    uint32_t* skipped = nullptr;  // [max_calls]: stages that launched nothing
 };
 std::mutex g_prof_mu;
 Profiler g_prof;
 
-// Events for the next profiled call (nullptr if none) and the stage mask.
-hipEvent_t* profile_slot(uint32_t* mask) {
+// Events for the next profiled call (nullptr if none), the stage mask and
+// the call's record of skipped stages.
+hipEvent_t* profile_slot(uint32_t* mask, uint32_t** skipped) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof.active || g_prof.calls >= g_prof.max_calls) return nullptr;
     *mask = g_prof.mask;
+    *skipped = g_prof.skipped + g_prof.calls;
+    **skipped = 0;
     return g_prof.ev + (size_t)(g_prof.calls++) * (MOE_NUM_STAGES + 1);
 }
 
@@ -270,9 +274,15 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     const void* residual = opts ? opts->residual : nullptr;
 
     uint32_t prof_mask = 0;
-    hipEvent_t* ev = profile_slot(&prof_mask);
+    uint32_t* prof_skipped = nullptr;
+    hipEvent_t* ev = profile_slot(&prof_mask, &prof_skipped);
     auto mark = [&](int i) {
         if (ev && boundary_needed(prof_mask, i)) (void)hipEventRecord(ev[i], stream);
+    };
+    // a stage that launches nothing reports no time (its two boundary events
+    // still bracket an empty interval of event overhead)
+    auto skip = [&](int s) {
+        if (ev) *prof_skipped |= 1u << s;
     };
     mark(0);
     LAUNCH(launch_router_topk(dtype, x, w_router, bias, Ti, di, Ei, ki, ids, gates, stream), "router_topk");
@@ -285,6 +295,7 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     // The streamed GEMM 1 reads x through row_token itself.
     const bool gather = !(dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM);
     if (gather) LAUNCH(launch_gather_rows(dtype, x, row_token, R, di, kb, x_perm, stream), "gather_rows");
+    else skip(2);
     mark(3);
     if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM) {
         LAUNCH(launch_gemm1_swiglu_stream(x, row_token, w1, w3, offsets, R, Ei, di, fi, plan.mf,
@@ -308,6 +319,8 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     mark(5);
     if (opts && opts->y_out)
         LAUNCH(launch_sum_splits(y, plan.splits, R, di, opts->y_out, stream), "sum_splits");
+    else
+        skip(5);
     mark(6);
     LAUNCH(launch_combine(dtype, y, plan.splits, gates, slot_row, residual, Ti, di, ki, R, out, stream), "combine");
     mark(7);
@@ -381,6 +394,7 @@ moe_status_t moe_ffn_profile_begin(int32_t max_calls, uint32_t stage_mask) {
         }
     }
     g_prof.ev = ev;
+    g_prof.skipped = new uint32_t[max_calls]();
     g_prof.max_calls = max_calls;
     g_prof.calls = 0;
     g_prof.mask = stage_mask == 0 ? (1u << MOE_NUM_STAGES) - 1 : stage_mask & ((1u << MOE_NUM_STAGES) - 1);
@@ -396,7 +410,7 @@ moe_status_t moe_ffn_profile_end(float* stage_ms, int32_t* calls) {
     for (int c = 0; c < g_prof.calls && st == MOE_OK; ++c) {
         hipEvent_t* e = g_prof.ev + (size_t)c * (MOE_NUM_STAGES + 1);
         for (int s = 0; s < MOE_NUM_STAGES; ++s) {
-            if (!((g_prof.mask >> s) & 1u)) continue;
+            if (!((g_prof.mask >> s) & 1u) || ((g_prof.skipped[c] >> s) & 1u)) continue;
             hipError_t r = hipEventSynchronize(e[s + 1]);
             if (r != hipSuccess) { st = hip_fail(r, "hipEventSynchronize"); break; }
             float ms = 0.0f;
@@ -408,6 +422,7 @@ moe_status_t moe_ffn_profile_end(float* stage_ms, int32_t* calls) {
     const size_t n = (size_t)g_prof.max_calls * (MOE_NUM_STAGES + 1);
     for (size_t i = 0; i < n; ++i) (void)hipEventDestroy(g_prof.ev[i]);
     delete[] g_prof.ev;
+    delete[] g_prof.skipped;
     const int recorded = g_prof.calls;
     const uint32_t mask = g_prof.mask;
     g_prof = Profiler();

@@ -125,3 +125,12 @@ def test_workspace_bytes(binding):
     assert floor <= n <= floor + R * d * 4 + 64 * 1024 * 1024
     assert binding.moe_ffn_workspace_bytes(4, 96, 128, 8, 2, binding.MOE_DTYPE_BF16) == 0
     assert binding.moe_ffn_workspace_bytes(64, 128, 256, 8, 2, binding.MOE_DTYPE_F32) > 0
+
+
+def test_profile_validation(binding):
+    # both paths return before any HIP call
+    assert binding.lib.moe_ffn_profile_end(None, None) == binding.MOE_ERR_INVALID_ARG
+    assert binding.lib.moe_ffn_profile_begin(0, 0) == binding.MOE_ERR_INVALID_ARG
+    assert binding.lib.moe_ffn_profile_begin(1000001, 0) == binding.MOE_ERR_INVALID_ARG
+    assert binding.moe_ffn_stage_name(3) == "gemm1_swiglu"
+    assert binding.moe_ffn_stage_name(binding.MOE_NUM_STAGES) == ""
