@@ -12,8 +12,9 @@
 // 1 KiB run.  For bf16 with E = 8 the matching router rows (8 rows of 8
 // experts, 128 contiguous bytes) are read straight from global memory, where
 // the 64 KiB router matrix stays L2-resident; other shapes read it element by
-// element.  Partial logits are summed across the lanes of a wave with a
-// butterfly of cross-lane adds, then across the 4 waves in LDS in a fixed
+// element.  The TPW x E partial logits of a lane are summed across the lanes
+// of a wave with a halving butterfly (each exchange step sends half as many
+// values as the one before), then across the 4 waves in LDS in a fixed
 // order, and lane tt of wave 0 selects and normalises token tt.
 //
 // Logits stay fp32 (products of bf16 inputs are exact in fp32, sums are
@@ -47,10 +48,38 @@ template <> struct Vec<float> {
     __device__ static float one(const float* p, size_t i) { return p[i]; }
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
+template <int NV>
+constexpr int log2_of() { return NV <= 1 ? 0 : 1 + log2_of<NV / 2>(); }
+
+// Sum each of NV = 2^m per-lane values over the 64 lanes of a wave.  At
+// offset o (32, 16, ...) the lane with bit o set keeps the upper half of its
+// remaining values and sends the lower half to its partner, which does the
+// reverse, so each step exchanges half as many values as the one before
+// (NV - 1 shuffles in all, then 6 - m single ones).  On return v[0] of lane L
+// holds the sum of value index (L >> (6 - m)) & (NV - 1).
+template <int NV, int S>
+__device__ __forceinline__ void wave_sum_step(float (&v)[NV], int lane) {
+    constexpr int off = 32 >> S;
+    constexpr int count = S < log2_of<NV>() ? (NV >> S) : 1;  // values still held
+    if constexpr (count > 1) {
+        constexpr int half = count / 2;
+        const bool upper = (lane & off) != 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+        for (int j = 0; j < half; ++j) {
+            const float send = upper ? v[j] : v[j + half];
+            const float keep = upper ? v[j + half] : v[j];
+            v[j] = keep + __shfl_xor(send, off, 64);
+        }
+    } else {
+        v[0] += __shfl_xor(v[0], off, 64);
+    }
+    if constexpr (S < 5) wave_sum_step<NV, S + 1>(v, lane);
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_sum_split(float (&v)[NV], int lane) {
+    static_assert(NV >= 1 && NV <= 64 && (NV & (NV - 1)) == 0, "NV must be a power of 2 up to 64");
+    wave_sum_step<NV, 0>(v, lane);
 }
 
 // ROWS8: bf16 router rows of exactly 8 experts, read as one 16-byte vector.
@@ -106,13 +135,17 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
         }
     }
 
+    // Wave sums of the TPW x EMAX partial logits (acc[tt][e] stays 0 for
+    // e >= E), value index tt * EMAX + e.
+    constexpr int NV = TPW * EMAX;
+    constexpr int SHIFT = 6 - log2_of<NV>();
+    float v[NV];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-        for (int e = 0; e < EMAX; ++e) {
-            const float v = (e < E) ? wave_sum(acc[tt][e]) : 0.0f;
-            if (lane == 0) part[wave][tt][e] = v;
-        }
+        for (int e = 0; e < EMAX; ++e) v[tt * EMAX + e] = acc[tt][e];
+    wave_sum_split<NV>(v, lane);
+    if ((lane & ((1 << SHIFT) - 1)) == 0) (&part[wave][0][0])[lane >> SHIFT] = v[0];
     __syncthreads();
     if (wave != 0 || lane >= TPW) return;
 
