@@ -217,11 +217,15 @@ hipError_t launch_t(const void* x, const void* wr, const float* bias, int T_, in
 template <typename T>
 hipError_t dispatch_e(const void* x, const void* wr, const float* bias, int T_, int d, int E,
                       int k, int32_t* ids, float* gates, hipStream_t stream) {
-    // Large batches share each router row load among 4 (or 2) tokens.
+    // Larger batches share each router row load among more tokens of a
+    // workgroup (measured on MI355X at d = 4096: 1 token per workgroup is
+    // fastest up to a few hundred tokens, 8 from a few thousand).
     const bool big = T_ > 1024;
     if constexpr (sizeof(T) == 2) {
         if (E == 8) {
-            if (big) return launch_t<T, 8, 4, true>(x, wr, bias, T_, d, E, k, ids, gates, stream);
+            if (T_ > 2048) return launch_t<T, 8, 8, true>(x, wr, bias, T_, d, E, k, ids, gates, stream);
+            if (T_ > 768) return launch_t<T, 8, 4, true>(x, wr, bias, T_, d, E, k, ids, gates, stream);
+            if (T_ > 384) return launch_t<T, 8, 2, true>(x, wr, bias, T_, d, E, k, ids, gates, stream);
             return launch_t<T, 8, 1, true>(x, wr, bias, T_, d, E, k, ids, gates, stream);
         }
     }

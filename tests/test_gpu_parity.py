@@ -51,6 +51,7 @@ SMALL = [
     (1100, 256, 384, 8, 2, torch.bfloat16),   # partial last row tiles, K split 2 in GEMM 2
     (600, 192, 320, 4, 2, torch.bfloat16),    # ragged columns in both GEMMs
     (2000, 128, 256, 8, 1, torch.bfloat16),   # k = 1, 250 rows per expert
+    (2101, 128, 256, 8, 2, torch.bfloat16),   # router with 8 tokens per workgroup, ragged last group
     # streamed-weight path (about a dozen rows or fewer per expert)
     (48, 192, 320, 8, 2, torch.bfloat16),     # ragged slabs, experts above 16 rows, K split 2
     (20, 256, 1024, 8, 2, torch.bfloat16),    # K split 8, one step per wave
