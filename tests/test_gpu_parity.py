@@ -236,12 +236,29 @@ def test_stack_workload_teacher_forced():
     x = torch.empty_like(h)
     rng = np.random.default_rng(3)
     total_ties = 0
+    # Free-running tokens: the oracle carries them through all the layers on
+    # its own, with the same bf16 storage of x and h as the GPU, and their
+    # final h is compared with the GPU's where their routing never differed.
+    free_tok = np.sort(rng.choice(T, size=8, replace=False))
+    free_idx = torch.as_tensor(free_tok, device=DEV)
+    h_free = inputs.host_array(h[free_idx])  # bf16 bits
+    diverged = np.zeros(len(free_tok), bool)
+
+    def bf16_bits(a):
+        return inputs.host_array(torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16))
+
     for layer in range(wl.layers):
         inp = inputs.make_weights(d, f, E, torch.bfloat16, DEV, 0, "stack", layer)
         binding.moe_rmsnorm(h, x, eps=wl.rms_eps)
         inp["x"] = x
         g = PT.run_gpu(inp, k, residual=h)
         host = PT.host_inputs(inp)
+        # free-running tokens: oracle layer on the oracle's own h
+        x_free = bf16_bits(oracle.rmsnorm(h_free, wl.rms_eps))
+        fr = oracle.moe_tokens(x_free, host["w_router"], host["w1"], host["w3"], host["w2"], k)
+        gpu_ids = PT.to_np(g["ids"])[free_tok]
+        diverged |= np.any(np.sort(fr["ids"], axis=1) != np.sort(gpu_ids, axis=1), axis=1)
+        h_free = bf16_bits(inputs.bf16_bits_to_f64(h_free) + fr["out"])
         tok = np.sort(rng.choice(T, size=6, replace=False))
         # RMSNorm of this layer's input, against the oracle
         h_tok = inputs.host_array(h[torch.as_tensor(tok, device=DEV)])
@@ -269,3 +286,15 @@ def test_stack_workload_teacher_forced():
         h = g["out"]
         del inp, host, g
     print("stack: %d near-tie tokens over %d layers" % (total_ties, wl.layers))
+    got = PT.out_f64(h[free_idx])
+    want = inputs.bf16_bits_to_f64(h_free)
+    keep = ~diverged
+    print("free-running: %d of %d tokens kept their routing through %d layers"
+          % (int(keep.sum()), len(free_tok), wl.layers))
+    if keep.any():
+        # Both sides round h to bf16 after every layer from slightly different
+        # sums, so the two h may drift apart by up to one bf16 unit (2^-8 of
+        # |h|) per layer; this reports the drift and bounds it linearly.
+        rel = np.abs(got[keep] - want[keep]).max() / np.abs(want[keep]).max()
+        print("free-running h_%d error on those tokens: %.2e of max|h|" % (wl.layers, rel))
+        assert rel <= wl.layers * 2.0 ** -8, rel
