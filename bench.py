@@ -13,7 +13,9 @@ and just after the dominant kernel (the w1/w3 grouped GEMM with the SwiGLU
 epilogue; moe_ffn_profile_begin/end), which gives its average duration over
 the timed region for the roofline entry.  A further, untimed pass records
 events at every stage boundary for the per-stage breakdown ("stages_ms";
-each boundary event adds a few microseconds there).
+each boundary event adds a few microseconds there), and another records HIP
+events around each step for the per-step median, minimum and 90th percentile
+("step_ms").
 
 The CPU baseline times the fp64 oracle on the host on a bounded sample of the
 same workload.
@@ -144,6 +146,18 @@ def run_workload(name, steps, warmup, binding, inputs, torch):
     torch.cuda.synchronize()
     stage_ms, calls = binding.moe_ffn_profile_end()
     stage_avg = {kk: v / calls for kk, v in stage_ms.items() if v > 0}  # skipped stages sum to 0
+    # Untimed distribution pass: HIP events around each step on the launch
+    # stream (the library launches on torch's current stream).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    step_dist = {"median": round(per[len(per) // 2], 5), "min": round(per[0], 5),
+                 "p90": round(per[min(len(per) - 1, int(0.9 * len(per)))], 5)}
 
     g_bytes, g_flops = gemm1_algorithmic(wl, counts_h)
     g_ms = timed_ms["gemm1_swiglu"] / steps
@@ -155,6 +169,7 @@ def run_workload(name, steps, warmup, binding, inputs, torch):
         "ms_per_step": ms_per_step,
         "tokens_per_s": wl.T / (ms_per_step * 1e-3),
         "stage_ms": {kk: round(v, 5) for kk, v in stage_avg.items()},  # breakdown pass
+        "step_ms": step_dist,  # distribution pass
         "counts": counts_h.tolist(),
         "gemm1_ms": g_ms,
         "gemm1_gbs": g_bytes / (g_ms * 1e-3) / 1e9,
@@ -558,6 +573,7 @@ def main():
                   "hbm_gbs": round(prim["layer_gbs"], 1),
                   "hbm_frac": round(prim["layer_gbs"] / HBM_PEAK_GBS, 4)},
         "stages_ms": prim["stage_ms"],
+        "step_ms": prim["step_ms"],
     }
     if args.secondary != "none" and args.secondary != args.workload:
         # free the primary inputs before the secondary workload
@@ -573,6 +589,7 @@ def main():
                       "mfma_frac": round(sec["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
                       "hbm_gbs": round(sec["layer_gbs"], 1)},
             "stages_ms": sec["stage_ms"],
+            "step_ms": sec["step_ms"],
         }
         prim["inp"] = prim_inp
     if args.sweep:

@@ -51,7 +51,7 @@ struct Plan {
     bool g1_ksplit = false;  // streamed GEMM 1: split K over the waves of a workgroup
     int mf = 1;              // streamed GEMMs: 16-row fragments per tile
     size_t ids = 0, gates = 0, counts = 0, offsets = 0, slot_row = 0, row_token = 0;
-    size_t x_perm = 0, h = 0, y = 0, total = 0;
+    size_t x_perm = 0, h = 0, y = 0, partials = 0, total = 0;
 };
 
 // Tile variant and K-split of the bf16 GEMMs, and the workspace layout.
@@ -89,13 +89,11 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
         } else if (tile_ok) {
             // (the 256-row tile kernels address x_perm, h and each weight
             // matrix with 32-bit buffer offsets: each must stay under 2 GiB)
-            // Many rows per expert: 256x256 macro tiles.  GEMM 2 has d/256
-            // column tiles; when that gives under ~4 workgroups per CU, cut
-            // its K range in two (partials summed by the combine).
+            // Many rows per expert: 256x256 macro tiles; each XCD's last
+            // partial round of tiles may be cut into K pieces, summed by a
+            // fixup kernel (y stays one slice).
             p.variant = GEMM_TILE256;
-            const int64_t nt2 = (d + 255) / 256;
-            const int64_t tiles = nt2 * ((R + 255) / 256 + E / 2);
-            p.splits = (tiles < 1024 && f / 64 >= 16) ? 2 : 1;
+            p.splits = 1;
         } else {
             // Operands past 2 GiB: 128-row tiles with 64-bit addressing.
             p.variant = (R <= 64 * E) ? GEMM_SMALL_M : GEMM_LARGE_M;
@@ -130,6 +128,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
     p.x_perm = take((size_t)R * d * es);
     p.h = take((size_t)R * f * es);
     p.y = take((size_t)p.splits * R * d * 4);
+    p.partials = p.variant == GEMM_TILE256 ? take(tile_partials_bytes((int)R, (int)E, (int)d, (int)f)) : 0;
     p.total = off;
     return p;
 }
@@ -304,9 +303,11 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
         mark(4);
         LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.mf, plan.splits, y, stream), "gemm2");
     } else if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_TILE256) {
-        LAUNCH(launch_gemm1_swiglu_tile(x_perm, w1, w3, offsets, R, Ei, di, fi, kb, h, stream), "gemm1_swiglu");
+        float* partials = reinterpret_cast<float*>(ws + plan.partials);
+        LAUNCH(launch_gemm1_swiglu_tile(x_perm, w1, w3, offsets, R, Ei, di, fi, kb, partials, h, stream),
+               "gemm1_swiglu");
         mark(4);
-        LAUNCH(launch_gemm2_tile(h, w2, offsets, R, Ei, fi, di, plan.splits, kb, y, stream), "gemm2");
+        LAUNCH(launch_gemm2_tile(h, w2, offsets, R, Ei, fi, di, kb, partials, y, stream), "gemm2");
     } else if (dtype == MOE_DTYPE_BF16) {
         LAUNCH(launch_gemm1_swiglu_bf16(plan.variant, x_perm, w1, w3, offsets, R, Ei, di, fi, h, stream), "gemm1_swiglu");
         mark(4);

@@ -71,14 +71,19 @@ hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* off
                                int f, int d, int mf, int splits, float* y, hipStream_t stream);
 
 // The same two contractions for batches with many rows per expert: 256x256
-// macro tiles, double-buffered LDS.
+// macro tiles staged through LDS.  In GEMM 2 each XCD's last, partial round
+// of tiles may be cut into K pieces whose fp32 partial sums go to `partials`
+// (tile_partials_bytes(R, E, d, f) bytes of scratch, also used by GEMM 1 for
+// a small header) and are summed, in piece order, by a second kernel that
+// stores y; launch_gemm2_tile makes both launches.
 // kb: A (x_perm) and the h output in the K-blocked layout
+size_t tile_partials_bytes(int R, int E, int d, int f);
 hipError_t launch_gemm1_swiglu_tile(const void* x_perm, const void* w1, const void* w3,
                                     const int32_t* offsets, int R, int E, int d, int f, int kb,
-                                    void* h, hipStream_t stream);
-// kb: A (h) in the K-blocked layout
+                                    float* partials, void* h, hipStream_t stream);
+// kb: A (h) in the K-blocked layout; y [R, d] fp32 (one slice)
 hipError_t launch_gemm2_tile(const void* h, const void* w2, const int32_t* offsets, int R, int E,
-                             int f, int d, int splits, int kb, float* y, hipStream_t stream);
+                             int f, int d, int kb, float* partials, float* y, hipStream_t stream);
 
 // out[t,:] = (residual[t,:] +) sum_j gates[t,j] * sum_s y[s][slot_row[t*k+j], :]
 hipError_t launch_combine(int dtype, const float* y, int splits, const float* gates,

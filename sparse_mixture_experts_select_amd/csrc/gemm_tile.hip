@@ -4,7 +4,7 @@
 // Same products as the other GEMM files (Mixtral of Experts, wikillm.com card,
 // "Method", SwiGLU pseudocode): per expert e over its grouped rows,
 //   GEMM 1:  h = SiLU(X_e . w1[e]) * (X_e . w3[e])
-//   GEMM 2:  y = h_e . w2[e]   (fp32, optionally in K slices)
+//   GEMM 2:  y = h_e . w2[e]   (fp32)
 //
 // Workgroup: 256 threads = 4 wavefronts in a 2x2 grid.  Macro tile: 256 rows x
 // 256 weight columns (GEMM 1: 128 columns of w1 and the same 128 of w3; GEMM 2:
@@ -25,8 +25,8 @@
 // bytes land at the wave's LDS base + 16 l).  SGPR buffer descriptors over A
 // and the expert's weights; each lane's byte offset is fixed for the whole
 // loop and a wave-uniform offset advances per K step.  Four LDS stages of
-// 40 KiB (a full tile uses 32 KiB of each), loads three K steps ahead.  The one barrier of a step sits half
-// way through its MFMAs: before it each wave waits for its own loads of the
+// 40 KiB (a full tile uses 32 KiB of each), loads three K steps ahead.  The
+// one barrier of a step sits half way through its MFMAs: before it each wave waits for its own loads of the
 // next stage (always exactly vmcnt(8), vmcnt(10) in a tail tile: past the
 // end the refills repeat the last step, valid addresses never read); after it the wave refills the
 // stage of the previous step and reads the next step's A fragments under the
@@ -53,18 +53,28 @@
 // The DMA lane order fixes the LDS address, so each lane simply loads the
 // global chunk that belongs at its swizzled LDS position.
 //
-// Order.  Tiles are numbered by expert, then K slice, then pairs of column
-// tiles; within a pair, the full-row tiles of the first column tile (m
-// fastest), those of the second, then the pair's tail tile.  Each XCD takes a
-// contiguous run of tile numbers (workgroup IDs are dealt to the 8 XCDs
-// round-robin), so workgroups that share a weight panel run together and
-// share one L2.
+// Order.  Tiles are numbered by expert, then pairs of column tiles; within a
+// pair, the full-row tiles of the first column tile (m fastest), those of
+// the second, then the pair's tail tile.  Each XCD takes a contiguous run of
+// ceil(n/8) tile numbers (workgroup IDs are dealt to the 8 XCDs round-robin),
+// so workgroups that share a weight panel run together and share one L2.
+//
+// Last round (GEMM 2).  An XCD's tiles run in rounds of its CUs; the tiles
+// of its last, partial round may be cut into p equal K ranges (p chosen per
+// XCD from a cost in K steps: rounds x (steps per piece + fill and epilogue)
+// + the partial sums' traffic), so that round keeps more CUs busy while all
+// workgroups still walk K in step.  A piece writes its fp32 accumulators to
+// a partial-sum slot; tile_fixup_kernel then sums the pieces of each cut
+// tile in piece order and stores y.  GEMM 1 tiles are never cut: with its
+// SwiGLU epilogue the fixup cost more than the rounds saved (measured).
 //
 // Epilogue.  GEMM 1 forms SiLU(a) * b, stages the bf16 tile in LDS (two of the
 // stage arrays, 16-byte chunks XOR-swizzled by row) and writes it with 16-byte
 // row-contiguous stores.  GEMM 2 writes fp32 straight from the
 // accumulators (64-byte row segments per fragment).
 #include "common.h"
+
+#include <atomic>
 
 namespace moe {
 namespace {
@@ -98,11 +108,219 @@ __device__ __forceinline__ void stage_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+constexpr int kMaxCpx = 32;      // CUs per XCD the schedule plans for (MI355X: 32)
+constexpr int kMaxPieces = 8;      // K pieces per cut tile (GEMM 2)
+constexpr int kPieceOverhead = 16;  // per-item cost in K steps: pipeline fill, epilogue
+constexpr int kPieceTraffic = 1;    // per-piece cost in K steps: its 256 KiB partial sum
+                                    // written and read back by the fixup (measured)
+constexpr int kSlotFloats = kThreads * 256;  // one tile's fp32 accumulators
+// The partial-sum buffer starts with a header written by the tile kernel for
+// the fixup: ints [8 x] = the number of cut tiles of XCD x, then from int 64
+// one 8-int descriptor per cut tile {row0, row_end, col0, is_tail, first
+// slot, pieces}, cut tiles numbered XCD by XCD.  The slots follow.
+constexpr int kHeaderFloats = 64 + 8 * 8 * kMaxCpx;
+
+// Geometry of tile t.  Tiles are numbered by expert, then pairs of column
+// tiles; within a pair, the full-row tiles of the first column tile (m
+// fastest), those of the second, then the pair's tail tile.  Per expert with
+// n_e rows: mt_n row tiles of 256 (the last one partial when more than 128
+// rows remain) per column tile, plus one tail tile per pair of column tiles
+// when 1..128 rows remain.
+struct TileGeo {
+    int e, row0, row_end, col0;
+    bool is_tail;
+};
+
+__device__ __forceinline__ int count_tiles(const int32_t* offsets, int E, int NT, int NTP) {
+    int n = 0;
+    for (int e = 0; e < E; ++e) {
+        const int n_e = offsets[e + 1] - offsets[e];
+        const int rem = n_e & (kBM - 1);
+        const int mt_n = (n_e >> 8) + (rem > 128 ? 1 : 0);
+        const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
+        n += mt_n * NT + tail * NTP;
+    }
+    return n;
+}
+
+__device__ __forceinline__ TileGeo tile_geometry(int t, const int32_t* offsets, int E, int NT,
+                                                 int NTP, int BN) {
+    TileGeo g{0, 0, 0, 0, false};
+    int L = t;
+    for (int e = 0; e < E; ++e) {
+        const int o0 = offsets[e];
+        const int n_e = offsets[e + 1] - o0;
+        const int rem = n_e & (kBM - 1);
+        const int mt_n = (n_e >> 8) + (rem > 128 ? 1 : 0);
+        const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
+        const int per_e = mt_n * NT + tail * NTP;
+        if (L < per_e) {
+            const int bs = 2 * mt_n + tail;  // tiles per pair of column tiles (the last
+                                             // pair has one column tile when NT is odd)
+            const int q = min(L / bs, NTP - 1);
+            const int r = L - q * bs;
+            const int n_in = (2 * q + 1 < NT) ? 2 : 1;
+            g.e = e;
+            if (r < mt_n * n_in) {
+                g.col0 = (2 * q + r / mt_n) * BN;
+                g.row0 = o0 + (r % mt_n) * kBM;
+            } else {
+                g.is_tail = true;
+                g.col0 = 2 * q * BN;
+                g.row0 = o0 + (n_e >> 8) * kBM;
+            }
+            g.row_end = o0 + n_e;
+            return g;
+        }
+        L -= per_e;
+    }
+    return g;
+}
+
+// Work of XCD x.  Workgroup IDs are dealt to the 8 XCDs round-robin, so XCD
+// x runs the workgroups with blockIdx % 8 == x; it gets the x-th run of
+// ceil(n/8) tile numbers (tiles sharing a weight panel then share one L2).  Its
+// first `full` tiles, whole rounds of its cpx CUs, run whole; the r left over
+// (fewer than cpx) are each cut into p equal K ranges when that finishes the
+// XCD's work sooner (fewer idle CUs in its last round), the pieces of one K
+// range of all r tiles running together.
+struct XcdSched {
+    int start, full, r, p;
+};
+
+__device__ __forceinline__ XcdSched xcd_schedule(int n_tiles, int x, int cpx, int KT, int max_pieces) {
+    XcdSched s;
+    const int per_xcd = (n_tiles + 7) / 8;
+    s.start = min(x * per_xcd, n_tiles);
+    const int n_x = min(s.start + per_xcd, n_tiles) - s.start;
+    s.full = (n_x / cpx) * cpx;
+    s.r = n_x - s.full;
+    s.p = 1;
+    if (s.r > 0) {
+        int best = (KT + kPieceOverhead);  // one round of whole tiles
+        for (int p = 2; p <= max_pieces; ++p) {
+            if (s.r * p > 2 * cpx || KT / p < 8) break;
+            const int cost = ((s.r * p + cpx - 1) / cpx) * ((KT + p - 1) / p + kPieceOverhead) +
+                             s.r * p * kPieceTraffic;
+            if (cost < best) {
+                best = cost;
+                s.p = p;
+            }
+        }
+    }
+    return s;
+}
+
+// First partial-sum slot and first cut-tile number of XCD x (the XCDs'
+// pieces and cut tiles are packed in XCD order).
+__device__ __forceinline__ int2 xcd_bases(int n_tiles, int x, int cpx, int KT, int max_pieces) {
+    int2 b = make_int2(0, 0);
+    for (int x2 = 0; x2 < x; ++x2) {
+        const XcdSched s = xcd_schedule(n_tiles, x2, cpx, KT, max_pieces);
+        if (s.p > 1) {
+            b.x += s.r * s.p;
+            b.y += s.r;
+        }
+    }
+    return b;
+}
+
+// ---- epilogue of one tile: lane holds rows 4*lgrp + r (r = 0..3) of column
+// lrow of each fragment.  st0 and st1 are two LDS arrays of at least 32 KiB
+// (GEMM 1 stages h through them).
+template <bool DUAL>
+__device__ __forceinline__ void tile_epilogue(const floatx4 (&acc)[8][8], const TileGeo& geo,
+                                              void* __restrict__ C, int R, int N, int kb,
+                                              unsigned char* st0, unsigned char* st1) {
+    constexpr int BN = DUAL ? 128 : 256;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int lrow = lane & 15;
+    const int lgrp = lane >> 4;
+    const int row0 = geo.row0, row_end = geo.row_end, col0 = geo.col0;
+    const bool is_tail = geo.is_tail;
+    if (DUAL) {
+        __syncthreads();  // every wave is done reading the stages
+        // Stage the wave pair's 128 x 128 bf16 block of h in LDS (wm = 0 in
+        // st0, wm = 1 in st1; full tile: rows 0..127 | 128..255, tail tile:
+        // first | second column tile), 256 bytes per row, 16-byte chunk ch of
+        // row r stored at ch ^ (r % 16).
+        uint16_t* hs_w = reinterpret_cast<uint16_t*>(wm == 0 ? st0 : st1);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * m + 4 * lgrp + r;  // within the block's 128 rows
+                    const int c = wn * 64 + 16 * n + lrow;
+                    const float hv = silu_f32(acc[m][n][r]) * acc[m][n + 4][r];
+                    hs_w[row * 128 + (((c >> 3) ^ (row & 15)) << 3) + (c & 7)] =
+                        (uint16_t)f32_to_bf16_bits(hv);
+                }
+        __syncthreads();
+        uint16_t* h = reinterpret_cast<uint16_t*>(C);
+        // staged row sr = 0..255: block sr/128, row sr%128 of that block
+        if (kb) {
+            // K-blocked h: for each block of 32 columns, consecutive rows are
+            // one contiguous run of 64-byte row pieces.
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int idx = tid + kThreads * q;
+                const int piece = idx & 3;        // 16-byte piece of the 64-byte row segment
+                const int sr = (idx >> 2) & 255;
+                const int b = idx >> 10;          // block of 32 columns within the 128
+                const int ch = 4 * b + piece;     // 16-byte chunk of the staged row
+                const int rr = sr & 127;
+                const int grow = row0 + (is_tail ? rr : sr);
+                const int gc = col0 + (is_tail ? (sr >> 7) * BN : 0) + ch * 8;
+                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(sr < 128 ? st0 : st1);
+                if (grow < row_end && gc < N)
+                    *reinterpret_cast<uint4*>(h + ((size_t)(gc >> 5) * R + grow) * 32 + (gc & 31)) =
+                        *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int idx = tid + kThreads * q;
+                const int sr = idx >> 4;    // 0..255
+                const int ch = idx & 15;    // 16-byte chunk of the row
+                const int rr = sr & 127;
+                const int grow = row0 + (is_tail ? rr : sr);
+                const int gc = col0 + (is_tail ? (sr >> 7) * BN : 0) + ch * 8;
+                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(sr < 128 ? st0 : st1);
+                if (grow < row_end && gc < N)
+                    *reinterpret_cast<uint4*>(h + (size_t)grow * N + gc) =
+                        *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
+            }
+        }
+    } else {
+        float* y = reinterpret_cast<float*>(C);
+        const int rbase = row0 + (is_tail ? 0 : wm * 128);
+        const int cbase = col0 + (is_tail ? wm * BN : 0) + wn * 128;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int grow = rbase + 16 * m + 4 * lgrp + r;
+                if (grow >= row_end) continue;
+#pragma unroll
+                for (int n = 0; n < 8; ++n) {
+                    const int gc = cbase + 16 * n + lrow;
+                    if (gc < N) y[(size_t)grow * N + gc] = acc[m][n][r];
+                }
+            }
+    }
+}
+
 template <bool DUAL>
 __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
-    void* __restrict__ C, const int32_t* __restrict__ offsets, int R, int E, int K, int N,
-    int splits, int kb) {
+    void* __restrict__ C, float* __restrict__ partials, const int32_t* __restrict__ offsets, int R,
+    int E, int K, int N, int cpx, int max_pieces, int kb) {
     constexpr int BN = DUAL ? 128 : 256;  // output columns per column tile
     // One array per stage: the compiler can then tell the stage being read
     // from the stages the DMA is writing, and does not wait for those loads.
@@ -111,54 +329,39 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     __shared__ __align__(16) unsigned char st2[kStageBytes];
     __shared__ __align__(16) unsigned char st3[kStageBytes];
 
-    // ---- tile lookup.  Per expert with n_e rows: mt_n row tiles of 256 (the
-    // last one partial when more than 128 rows remain) per column tile, plus
-    // one tail tile per pair of column tiles when 1..128 rows remain.
+    // ---- this workgroup's item: a whole tile, or one K piece of a tile
     const int NT = (N + BN - 1) / BN;
     const int NTP = (NT + 1) / 2;
-    int total = 0;
-    for (int e = 0; e < E; ++e) {
-        const int n_e = offsets[e + 1] - offsets[e];
-        const int rem = n_e & (kBM - 1);
-        const int mt_n = (n_e >> 8) + (rem > 128 ? 1 : 0);
-        const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
-        total += (mt_n * NT + tail * NTP) * splits;
-    }
-    const int per_xcd = (total + 7) / 8;
+    const int KT = K / kBK;
+    const int n_tiles = count_tiles(offsets, E, NT, NTP);
+    const int xcd = blockIdx.x & 7;
     const int slot = blockIdx.x >> 3;
-    if (slot >= per_xcd) return;
-    int L = (blockIdx.x & 7) * per_xcd + slot;
-    if (L >= total) return;
-    int e = 0, row0 = 0, row_end = 0, col0 = 0, split = 0;
-    bool is_tail = false;
-    for (e = 0; e < E; ++e) {
-        const int o0 = offsets[e];
-        const int n_e = offsets[e + 1] - o0;
-        const int rem = n_e & (kBM - 1);
-        const int mt_n = (n_e >> 8) + (rem > 128 ? 1 : 0);
-        const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
-        const int per_split = mt_n * NT + tail * NTP;
-        if (L < per_split * splits) {
-            split = L / per_split;
-            const int Lr = L - split * per_split;
-            const int bs = 2 * mt_n + tail;  // tiles per pair of column tiles (the last
-                                             // pair has one column tile when NT is odd)
-            const int q = min(Lr / bs, NTP - 1);
-            const int r = Lr - q * bs;
-            const int n_in = (2 * q + 1 < NT) ? 2 : 1;
-            if (r < mt_n * n_in) {
-                col0 = (2 * q + r / mt_n) * BN;
-                row0 = o0 + (r % mt_n) * kBM;
-            } else {
-                is_tail = true;
-                col0 = 2 * q * BN;
-                row0 = o0 + (n_e >> 8) * kBM;
-            }
-            row_end = o0 + n_e;
-            break;
-        }
-        L -= per_split * splits;
+    if (DUAL) {
+        // GEMM 1: whole tiles only (no schedule, no partial sums)
+        const int per_xcd = (n_tiles + 7) / 8;
+        if (slot >= per_xcd || xcd * per_xcd + slot >= n_tiles) return;
     }
+    const XcdSched sc = DUAL ? XcdSched{xcd * ((n_tiles + 7) / 8), n_tiles, 0, 1}
+                             : xcd_schedule(n_tiles, xcd, cpx, KT, max_pieces);
+    if (!DUAL && slot == 0 && threadIdx.x == 0)
+        reinterpret_cast<int*>(partials)[8 * xcd] = sc.p > 1 ? sc.r : 0;
+    if (slot >= sc.full + sc.r * sc.p) return;
+    int t, kt0 = 0, kt1 = KT, piece = -1, rt = 0;
+    if (slot < sc.full) {
+        t = sc.start + slot;
+    } else {
+        const int u = slot - sc.full;
+        rt = u % sc.r;
+        t = sc.start + sc.full + rt;
+        if (sc.p > 1) {
+            piece = u / sc.r;
+            kt0 = piece * KT / sc.p;
+            kt1 = (piece + 1) * KT / sc.p;
+        }
+    }
+    const TileGeo geo = tile_geometry(t, offsets, E, NT, NTP, BN);
+    const int e = geo.e, row0 = geo.row0, row_end = geo.row_end, col0 = geo.col0;
+    const bool is_tail = geo.is_tail;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -168,10 +371,6 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     const int lrow = lane & 15;
     const int lgrp = lane >> 4;
 
-    const int KT = K / kBK;
-    const int kt_per = (KT + splits - 1) / splits;
-    const int kt0 = min(split * kt_per, KT);
-    const int kt1 = min(kt0 + kt_per, KT);
 
     // ---- DMA sources.  Buffer descriptors (SGPRs) over A and over the
     // expert's weight matrices; per lane a loop-invariant byte offset, per K
@@ -397,109 +596,142 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     // No load may still be writing LDS when the stages are reused below.
     MOE_WAIT_VM(0);
 
-    // ---- epilogue: lane holds rows 4*lgrp + r (r = 0..3) of column lrow of each fragment.
-    if (DUAL) {
-        __syncthreads();  // every wave is done reading the stages
-        // Stage the wave pair's 128 x 128 bf16 block of h in LDS (wm = 0 in
-        // st0, wm = 1 in st1; full tile: rows 0..127 | 128..255, tail tile:
-        // first | second column tile), 256 bytes per row, 16-byte chunk ch of
-        // row r stored at ch ^ (r % 16).
-        uint16_t* hs_w = reinterpret_cast<uint16_t*>(wm == 0 ? st0 : st1);
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * m + 4 * lgrp + r;  // within the block's 128 rows
-                    const int c = wn * 64 + 16 * n + lrow;
-                    const float hv = silu_f32(acc[m][n][r]) * acc[m][n + 4][r];
-                    hs_w[row * 128 + (((c >> 3) ^ (row & 15)) << 3) + (c & 7)] =
-                        (uint16_t)f32_to_bf16_bits(hv);
-                }
-        __syncthreads();
-        uint16_t* h = reinterpret_cast<uint16_t*>(C);
-        // staged row sr = 0..255: block sr/128, row sr%128 of that block
-        if (kb) {
-            // K-blocked h: for each block of 32 columns, consecutive rows are
-            // one contiguous run of 64-byte row pieces.
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int idx = tid + kThreads * q;
-                const int piece = idx & 3;        // 16-byte piece of the 64-byte row segment
-                const int sr = (idx >> 2) & 255;
-                const int b = idx >> 10;          // block of 32 columns within the 128
-                const int ch = 4 * b + piece;     // 16-byte chunk of the staged row
-                const int rr = sr & 127;
-                const int grow = row0 + (is_tail ? rr : sr);
-                const int gc = col0 + (is_tail ? (sr >> 7) * BN : 0) + ch * 8;
-                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(sr < 128 ? st0 : st1);
-                if (grow < row_end && gc < N)
-                    *reinterpret_cast<uint4*>(h + ((size_t)(gc >> 5) * R + grow) * 32 + (gc & 31)) =
-                        *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int idx = tid + kThreads * q;
-                const int sr = idx >> 4;    // 0..255
-                const int ch = idx & 15;    // 16-byte chunk of the row
-                const int rr = sr & 127;
-                const int grow = row0 + (is_tail ? rr : sr);
-                const int gc = col0 + (is_tail ? (sr >> 7) * BN : 0) + ch * 8;
-                const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(sr < 128 ? st0 : st1);
-                if (grow < row_end && gc < N)
-                    *reinterpret_cast<uint4*>(h + (size_t)grow * N + gc) =
-                        *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
-            }
-        }
+    if (DUAL || piece < 0) {
+        tile_epilogue<DUAL>(acc, geo, C, R, N, kb, st0, st1);
     } else {
-        float* y = reinterpret_cast<float*>(C) + (size_t)split * R * N;
-        const int rbase = row0 + (is_tail ? 0 : wm * 128);
-        const int cbase = col0 + (is_tail ? wm * BN : 0) + wn * 128;
+        // a K piece: its fp32 accumulators go to a partial-sum slot laid out
+        // as the tile itself, row-major: 256 rows x 256 columns, or 128 rows
+        // x 512 columns (both column tiles) for a tail tile
+        const int2 bases = xcd_bases(n_tiles, xcd, cpx, KT, max_pieces);
+        const int first_slot = bases.x + rt * sc.p;
+        if (piece == 0 && threadIdx.x == 0) {
+            int* desc = reinterpret_cast<int*>(partials) + 64 + 8 * (bases.y + rt);
+            desc[0] = row0;
+            desc[1] = row_end;
+            desc[2] = col0;
+            desc[3] = is_tail ? 1 : 0;
+            desc[4] = first_slot;
+            desc[5] = sc.p;
+        }
+        float* dst = partials + kHeaderFloats + (size_t)(first_slot + piece) * kSlotFloats;
+        const int lane = threadIdx.x & 63;
+        const int wave = threadIdx.x >> 6;
+        const int wm = wave >> 1, wn = wave & 1, lrow = lane & 15, lgrp = lane >> 4;
+        const int width = is_tail ? 512 : 256;
+        const int rbase = (is_tail ? 0 : wm * 128) + 4 * lgrp;
+        const int cbase = (is_tail ? wm * 256 : 0) + wn * 128 + lrow;
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int grow = rbase + 16 * m + 4 * lgrp + r;
-                if (grow >= row_end) continue;
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const int gc = cbase + 16 * n + lrow;
-                    if (gc < N) y[(size_t)grow * N + gc] = acc[m][n][r];
-                }
-            }
+                for (int n = 0; n < 8; ++n)
+                    dst[(rbase + 16 * m + r) * width + cbase + 16 * n] = acc[m][n][r];
     }
 }
 
+// GEMM 2's tiles cut into K pieces: sum the pieces' partial sums in piece
+// order and store y.  Elementwise over the cut tiles (their descriptors come
+// from the header): work unit = (cut tile, 256 float4 of its row-major sums),
+// so loads and y stores are 16-byte, row-contiguous and coalesced, and the
+// loads of every piece are in flight together.
+__global__ __launch_bounds__(kThreads) void tile_fixup_kernel(const float* __restrict__ partials,
+                                                              float* __restrict__ y, int N) {
+    constexpr int UNITS = kSlotFloats / 4 / kThreads;  // 64 work units per cut tile
+    const int* hdr = reinterpret_cast<const int*>(partials);
+    int n_cut = 0;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) n_cut += hdr[8 * x];
+    for (int w = blockIdx.x; w < n_cut * UNITS; w += gridDim.x) {
+        const int g = w / UNITS;  // cut tile
+        const int c = w - g * UNITS;
+        const int* desc = hdr + 64 + 8 * g;
+        const int row0 = desc[0], row_end = desc[1], col0 = desc[2], is_tail = desc[3];
+        const int first_slot = desc[4], p = desc[5];
+        const float4* src = reinterpret_cast<const float4*>(partials + kHeaderFloats) +
+                            (size_t)first_slot * (kSlotFloats / 4);
+        const int i = c * kThreads + threadIdx.x;  // float4 of the tile
+        float4 a = src[i];
+        for (int j = 1; j < p; ++j) {
+            const float4 v = src[(size_t)j * (kSlotFloats / 4) + i];
+            a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+        }
+        const int width4 = is_tail ? 128 : 64;  // float4 per tile row
+        const int grow = row0 + i / width4;
+        const int gc = col0 + 4 * (i % width4);
+        if (grow < row_end && gc < N) *reinterpret_cast<float4*>(y + (size_t)grow * N + gc) = a;
+    }
+}
+
+// Workgroups of a persistent launch: the current device's CU count, rounded
+// down to a multiple of 8 (queried once per device).
+int cus_per_xcd() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kMaxCpx;
+    int c = cached[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 8 * kMaxCpx;
+        c = n / 8;
+        if (c < 1) c = 1;
+        if (c > kMaxCpx) c = kMaxCpx;
+        cached[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
 template <bool DUAL>
-hipError_t launch_tile(const void* A, const void* B0, const void* B1, void* C,
-                       const int32_t* offsets, int R, int E, int K, int N, int splits, int kb,
+hipError_t launch_tile(const void* A, const void* B0, const void* B1, void* C, float* partials,
+                       const int32_t* offsets, int R, int E, int K, int N, int kb,
                        hipStream_t stream) {
     const long long BN = DUAL ? 128 : 256;
     const long long NT = (N + BN - 1) / BN;
     // bound on the tile count: per expert at most ceil(n_e / 256) row tiles
     // per column tile (a tail tile covers two column tiles)
     const long long mtiles = (R + kBM - 1) / kBM + E;
-    long long grid = mtiles * NT * splits;
-    grid = (grid + 7) / 8 * 8;
+    const long long n_max = mtiles * NT;
+    const int cpx = cus_per_xcd();
+    // GEMM 1 tiles are never cut: the SwiGLU fixup of cut tiles cost more than
+    // the rounds it saved (measured at T = 1024 .. 4096).
+    const int max_pieces = DUAL ? 1 : kMaxPieces;
+    // per XCD: its eighth of the tiles, plus at most 2 cpx extra pieces when
+    // tiles may be cut (a workgroup past the XCD's items exits at once, but
+    // still waits for a free CU: its LDS is a whole CU's)
+    const long long grid = 8 * ((n_max + 7) / 8 + (max_pieces > 1 ? 2 * cpx : 0));
     hipLaunchKernelGGL((tile_gemm_kernel<DUAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const bf16*>(A), reinterpret_cast<const bf16*>(B0),
-                       reinterpret_cast<const bf16*>(B1), C, offsets, R, E, K, N, splits, kb);
+                       reinterpret_cast<const bf16*>(B1), C, partials, offsets, R, E, K, N, cpx, max_pieces, kb);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || DUAL) return err;
+    // GEMM 2's cut tiles: at most 8 (cpx - 1) of 64 units each, one
+    // workgroup per unit (the ones past the cut tiles exit at once)
+    const unsigned fix_grid = (unsigned)(8 * cpx * (kSlotFloats / 4 / kThreads));
+    hipLaunchKernelGGL(tile_fixup_kernel, dim3(fix_grid), dim3(kThreads), 0, stream, partials,
+                       reinterpret_cast<float*>(C), N);
     return hipGetLastError();
 }
 
 }  // namespace
 
+size_t tile_partials_bytes(int R, int E, int d, int f) {
+    // at most 2 cpx pieces per XCD, and at most kMaxPieces per tile
+    const long long mtiles = (R + kBM - 1) / kBM + E;
+    const long long nt = (f + 127) / 128 > (d + 255) / 256 ? (f + 127) / 128 : (d + 255) / 256;
+    long long slots = 8 * 2 * (long long)kMaxCpx;
+    if (mtiles * nt * kMaxPieces < slots) slots = mtiles * nt * kMaxPieces;
+    return ((size_t)slots * kSlotFloats + kHeaderFloats) * sizeof(float);
+}
+
 hipError_t launch_gemm1_swiglu_tile(const void* x_perm, const void* w1, const void* w3,
                                     const int32_t* offsets, int R, int E, int d, int f, int kb,
-                                    void* h, hipStream_t stream) {
-    return launch_tile<true>(x_perm, w1, w3, h, offsets, R, E, d, f, 1, kb, stream);
+                                    float* partials, void* h, hipStream_t stream) {
+    return launch_tile<true>(x_perm, w1, w3, h, partials, offsets, R, E, d, f, kb, stream);
 }
 
 hipError_t launch_gemm2_tile(const void* h, const void* w2, const int32_t* offsets, int R, int E,
-                             int f, int d, int splits, int kb, float* y, hipStream_t stream) {
-    return launch_tile<false>(h, w2, nullptr, y, offsets, R, E, f, d, splits, kb, stream);
+                             int f, int d, int kb, float* partials, float* y, hipStream_t stream) {
+    return launch_tile<false>(h, w2, nullptr, y, partials, offsets, R, E, f, d, kb, stream);
 }
 
 }  // namespace moe
