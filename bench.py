@@ -5,7 +5,8 @@ Prints ONE JSON line on stdout.  A step is one full layer call
 of synthetic inputs that are already resident in HBM.  The primary workload is
 the T=32 decode batch at Mixtral shapes (d=4096, f=14336, E=8, k=2, bf16),
 which is HBM-bound; the T=4096 prefill batch (MFMA-bound) is reported beside
-it under "secondary".
+it under "secondary", the T=16384 batch with skewed routing under "skewed"
+and the 32-block stack under "stack".
 
 Live timing: the K timed steps are bracketed by torch.cuda.synchronize();
 inside them the library records HIP events on the launch stream just before
@@ -47,7 +48,8 @@ GEMM1_KERNEL = {
 }
 CALIBRATION_BYTES = 1 << 30
 PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d gpurun_out/pmc_{tag} -o run -- "
-               "python3 bench.py --steps 3 --warmup 1 --stack off --no-cpu-baseline --calibrate-copy")
+               "python3 bench.py --steps 3 --warmup 1 --stack off --skewed off --no-cpu-baseline "
+               "--calibrate-copy")
 TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o run -- "
                  "python3 bench.py --steps 10 --warmup 2 --cpu-seconds 2")
 
@@ -478,7 +480,7 @@ def _short_kernel_name(name):
 def summarize_trace(trace_dir):
     """Condense the --kernel-trace output of TRACE_COMMAND into
     profiles/moe_layer_decode_prefill_stack_kernel_stats.txt: per kernel and grid
-    size (which tells the decode launches from the prefill ones) the number of
+    size (which tells the workloads' launches apart) the number of
     calls and the average / min / max duration."""
     import csv
     import statistics
@@ -495,8 +497,8 @@ def summarize_trace(trace_dir):
     out = os.path.join(ROOT, "profiles", "moe_layer_decode_prefill_stack_kernel_stats.txt")
     with open(out, "w") as fh:
         fh.write("# rocprofv3 kernel trace of the benchmark: decode (T=32), prefill (T=4096), "
-                 "then the 32-block stack (T=2048; rmsnorm + layer per block); d=4096 f=14336 "
-                 "E=8 k=2 bf16\n")
+                 "skewed routing (T=16384), then the 32-block stack (T=2048; rmsnorm + layer per "
+                 "block); d=4096 f=14336 E=8 k=2 bf16\n")
         fh.write("# command: %s\n" % TRACE_COMMAND)
         fh.write("# summarized by: python3 bench.py --summarize-trace gpurun_out/trace\n")
         fh.write("# calls = warm-up + one routing probe call + timed steps; durations in us; "
@@ -518,6 +520,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skewed"])
     ap.add_argument("--secondary", default="prefill", choices=["prefill", "decode", "skewed", "none"])
+    ap.add_argument("--skewed", default="on", choices=["on", "off"],
+                    help="also run the skewed-routing workload (T=16384, biased router)")
     ap.add_argument("--stack", default="on", choices=["on", "off"],
                     help="also time the 32-block stack (90 GB of weights resident)")
     ap.add_argument("--sweep", action="store_true",
@@ -575,23 +579,33 @@ def main():
         "stages_ms": prim["stage_ms"],
         "step_ms": prim["step_ms"],
     }
-    if args.secondary != "none" and args.secondary != args.workload:
-        # free the primary inputs before the secondary workload
+    def side_workload(name):
+        # free the primary inputs while another workload runs
         prim_inp = prim.pop("inp")
-        sec = run_workload(args.secondary, args.steps, args.warmup, binding, inputs, torch)
-        sbound = "hbm" if args.secondary == "decode" else "mfma"
-        sec.pop("inp")
-        rec["secondary"] = {
-            "workload": args.secondary, "value": round(sec["tokens_per_s"], 1), "unit": "tokens/s",
-            "ms_per_step": round(sec["ms_per_step"], 5),
-            "roofline": roofline(sec, sbound),
-            "layer": {"tflops_active": round(sec["layer_tflops"], 2),
-                      "mfma_frac": round(sec["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                      "hbm_gbs": round(sec["layer_gbs"], 1)},
-            "stages_ms": sec["stage_ms"],
-            "step_ms": sec["step_ms"],
-        }
+        torch.cuda.empty_cache()
+        res = run_workload(name, args.steps, args.warmup, binding, inputs, torch)
+        res.pop("inp")
+        torch.cuda.empty_cache()
         prim["inp"] = prim_inp
+        out = {
+            "workload": name, "value": round(res["tokens_per_s"], 1), "unit": "tokens/s",
+            "ms_per_step": round(res["ms_per_step"], 5),
+            "roofline": roofline(res, "hbm" if name == "decode" else "mfma"),
+            "layer": {"tflops_active": round(res["layer_tflops"], 2),
+                      "mfma_frac": round(res["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "hbm_gbs": round(res["layer_gbs"], 1)},
+            "stages_ms": res["stage_ms"],
+            "step_ms": res["step_ms"],
+        }
+        if name == "skewed":
+            c = res["counts"]
+            out["expert_share"] = [round(v / sum(c), 4) for v in c]
+        return out
+
+    if args.secondary != "none" and args.secondary != args.workload:
+        rec["secondary"] = side_workload(args.secondary)
+    if args.skewed == "on" and args.workload != "skewed" and args.secondary != "skewed":
+        rec["skewed"] = side_workload("skewed")
     if args.sweep:
         prim_inp = prim.pop("inp")
         del prim_inp
