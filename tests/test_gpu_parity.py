@@ -58,7 +58,10 @@ SMALL = [
     (5, 128, 128, 64, 8, torch.bfloat16),     # E = 64, most experts empty
     (2, 256, 1024, 8, 2, torch.bfloat16),     # GEMM 1 with K split over the waves
     (110, 192, 320, 8, 2, torch.bfloat16),    # streamed, 2 row fragments per tile, ragged slabs
-    (200, 256, 512, 8, 2, torch.bfloat16),    # streamed, 4 row fragments per tile
+    (150, 256, 512, 8, 2, torch.bfloat16),    # streamed, 4 row fragments per tile
+    (200, 256, 512, 8, 2, torch.bfloat16),    # 256-row tiles: tail tiles only, GEMM 2 tiles cut in 2 K pieces
+    (600, 512, 1024, 8, 2, torch.bfloat16),   # GEMM 2's last round cut into 4 K pieces (fixup sums them)
+    (1500, 1024, 2048, 8, 2, torch.bfloat16), # GEMM 2 tiles cut into 3 K pieces, several per XCD
     (50, 100, 60, 5, 2, torch.float32),
     (200, 64, 96, 16, 4, torch.float32),
 ]
