@@ -50,7 +50,7 @@ struct Plan {
     int splits = 1;
     bool g1_ksplit = false;  // streamed GEMM 1: split K over the waves of a workgroup
     int mf = 1;              // streamed GEMMs: 16-row fragments per tile
-    size_t ids = 0, gates = 0, counts = 0, offsets = 0, slot_row = 0, row_token = 0;
+    size_t ids = 0, gates = 0, counts = 0, offsets = 0, slot_row = 0, row_token = 0, scan = 0;
     size_t x_perm = 0, h = 0, y = 0, partials = 0, total = 0;
 };
 
@@ -125,6 +125,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
     p.offsets = take((size_t)(E + 1) * 4);
     p.slot_row = take((size_t)R * 4);
     p.row_token = take((size_t)R * 4);
+    p.scan = take(route_scan_scratch_bytes((int)R, (int)E));
     p.x_perm = take((size_t)R * d * es);
     p.h = take((size_t)R * f * es);
     p.y = take((size_t)p.splits * R * d * 4);
@@ -286,7 +287,9 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     mark(0);
     LAUNCH(launch_router_topk(dtype, x, w_router, bias, Ti, di, Ei, ki, ids, gates, stream), "router_topk");
     mark(1);
-    LAUNCH(launch_route_scan(ids, Ti, ki, Ei, counts, offsets, slot_row, row_token, stream), "route_scan");
+    LAUNCH(launch_route_scan(ids, Ti, ki, Ei, counts, offsets, slot_row, row_token,
+                             reinterpret_cast<int32_t*>(ws + plan.scan), stream),
+           "route_scan");
     mark(2);
     // The 256-row tile GEMMs read x_perm and h in a K-blocked layout (see
     // gemm_tile.hip); a caller asking for h gets it row-major instead.

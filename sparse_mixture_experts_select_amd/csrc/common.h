@@ -35,9 +35,11 @@ hipError_t launch_router_topk(int dtype, const void* x, const void* w_router, co
                               int T, int d, int E, int k, int32_t* ids, float* gates,
                               hipStream_t stream);
 
+// scratch: route_scan_scratch_bytes(T * k, E) bytes (0: may be null)
+size_t route_scan_scratch_bytes(int R, int E);
 hipError_t launch_route_scan(const int32_t* ids, int T, int k, int E, int32_t* counts,
                              int32_t* offsets, int32_t* slot_row, int32_t* row_token,
-                             hipStream_t stream);
+                             int32_t* scratch, hipStream_t stream);
 
 // kb: write x_perm in the K-blocked layout of the 256-row tile GEMM (bf16)
 hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token, int R, int d,

@@ -17,6 +17,13 @@
 // pass 2 walks the same chunks again and gives each assignment its row as
 // (expert base + wave base + rank among earlier equal lanes).
 //
+// Past kScanSingleMax assignments the same two passes run over many
+// workgroups instead of one: route_count_kernel writes each workgroup's
+// per-expert counts of its contiguous block of assignments; route_place_kernel
+// reads all of them, forms the expert offsets and its block's base per expert
+// (the counts of the blocks before it), and ranks its block's assignments
+// exactly as the single-workgroup kernel does, so the grouping is identical.
+//
 // gather_rows_kernel then copies x[row_token[r]] into x_perm[r] with 16-byte
 // loads and stores, one row per wave iteration, so every read of a token row
 // is a contiguous, coalesced stream.
@@ -28,6 +35,8 @@ namespace {
 constexpr int kScanThreads = 1024;
 constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kBatch = 8;  // chunks of 64 ids loaded together per wave
+// above this many assignments the multi-workgroup form runs
+constexpr int kScanSingleMax = 4096;
 
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     const int32_t* __restrict__ ids, int R, int k, int E, int32_t* __restrict__ counts,
@@ -122,6 +131,129 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     }
 }
 
+constexpr int kBlockThreads = 256;
+constexpr int kBlockWaves = kBlockThreads / 64;
+constexpr int kBlockChunks = 4;                            // chunks of 64 per wave
+constexpr int kBlockIds = kBlockWaves * kBlockChunks * 64;  // assignments per workgroup
+
+// Per-expert counts of workgroup b's assignments [b * kBlockIds, ...).
+__global__ __launch_bounds__(kBlockThreads) void route_count_kernel(const int32_t* __restrict__ ids,
+                                                                     int R, int E,
+                                                                     int32_t* __restrict__ blk_counts) {
+    __shared__ int wave_count[kBlockWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c0 = blockIdx.x * kBlockWaves * kBlockChunks + wave * kBlockChunks;
+    int eb[kBlockChunks];
+#pragma unroll
+    for (int u = 0; u < kBlockChunks; ++u) {
+        const int a = (c0 + u) * 64 + lane;
+        eb[u] = a < R ? ids[a] : -1;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < kBlockChunks; ++u)
+        for (int ex = 0; ex < E; ++ex) {
+            const uint64_t m = __ballot(eb[u] == ex);
+            if (lane == ex) mine += __popcll(m);
+        }
+    wave_count[wave][lane] = mine;
+    __syncthreads();
+    if (threadIdx.x < 64 && threadIdx.x < E) {
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < kBlockWaves; ++w) tot += wave_count[w][threadIdx.x];
+        blk_counts[(size_t)blockIdx.x * E + threadIdx.x] = tot;
+    }
+}
+
+// Rows of workgroup b's assignments: expert base + the counts of the blocks
+// before b + the wave's base in the block + the rank among earlier equal
+// lanes.  Workgroup 0 also writes counts and offsets.
+__global__ __launch_bounds__(kBlockThreads) void route_place_kernel(
+    const int32_t* __restrict__ ids, int R, int k, int E, int nblk,
+    const int32_t* __restrict__ blk_counts, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot_row, int32_t* __restrict__ row_token) {
+    __shared__ int wave_count[kBlockWaves][64];
+    __shared__ int base_s[64];
+    __shared__ int total_s[64];
+    __shared__ int before_s[64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    if (threadIdx.x < 64) {
+        total_s[threadIdx.x] = 0;
+        before_s[threadIdx.x] = 0;
+    }
+    __syncthreads();
+    // every block's counts, summed per expert (integer sums: any order)
+    for (int i = threadIdx.x; i < nblk * E; i += kBlockThreads) {
+        const int b = i / E;
+        const int e = i - b * E;
+        const int c = blk_counts[i];
+        atomicAdd(&total_s[e], c);
+        if (b < (int)blockIdx.x) atomicAdd(&before_s[e], c);
+    }
+    const int c0 = blockIdx.x * kBlockWaves * kBlockChunks + wave * kBlockChunks;
+    int eb[kBlockChunks];
+#pragma unroll
+    for (int u = 0; u < kBlockChunks; ++u) {
+        const int a = (c0 + u) * 64 + lane;
+        eb[u] = a < R ? ids[a] : -1;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < kBlockChunks; ++u)
+        for (int ex = 0; ex < E; ++ex) {
+            const uint64_t m = __ballot(eb[u] == ex);
+            if (lane == ex) mine += __popcll(m);
+        }
+    wave_count[wave][lane] = mine;
+    __syncthreads();
+    if (wave == 0) {
+        // lane e: total of expert e and the part before this block
+        const int total = lane < E ? total_s[lane] : 0;
+        const int before = lane < E ? before_s[lane] : 0;
+        int incl = total;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
+        }
+        const int excl = incl - total;
+        if (lane < E) base_s[lane] = excl + before;
+        if (blockIdx.x == 0) {
+            if (lane < E) {
+                counts[lane] = total;
+                offsets[lane] = excl;
+            }
+            if (lane == E - 1) offsets[E] = incl;
+        }
+    }
+    __syncthreads();
+    // this wave's base per expert: block base + the waves before it
+    int next = 0;
+    if (lane < E) {
+        next = base_s[lane];
+        for (int w = 0; w < wave; ++w) next += wave_count[w][lane];
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int u = 0; u < kBlockChunks; ++u) {
+        const int a = (c0 + u) * 64 + lane;
+        const int e = eb[u];
+        int row = -1;
+        for (int ex = 0; ex < E; ++ex) {
+            const uint64_t m = __ballot(e == ex);
+            const int base = __shfl(next, ex, 64);
+            if (e == ex) row = base + __popcll(m & below);
+            if (lane == ex) next += __popcll(m);
+        }
+        if (e >= 0) {
+            slot_row[a] = row;
+            row_token[row] = a / k;
+        }
+    }
+}
+
 template <int VEC_BYTES>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
                                                           const int32_t* __restrict__ row_token,
@@ -170,11 +302,27 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float4* __restric
 
 }  // namespace
 
+size_t route_scan_scratch_bytes(int R, int E) {
+    if (R <= kScanSingleMax) return 0;
+    return (size_t)((R + kBlockIds - 1) / kBlockIds) * E * sizeof(int32_t);
+}
+
 hipError_t launch_route_scan(const int32_t* ids, int T, int k, int E, int32_t* counts,
                              int32_t* offsets, int32_t* slot_row, int32_t* row_token,
-                             hipStream_t stream) {
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, ids, T * k, k, E,
-                       counts, offsets, slot_row, row_token);
+                             int32_t* scratch, hipStream_t stream) {
+    const int R = T * k;
+    if (R <= kScanSingleMax) {
+        hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, ids, R, k, E,
+                           counts, offsets, slot_row, row_token);
+        return hipGetLastError();
+    }
+    const int nblk = (R + kBlockIds - 1) / kBlockIds;
+    hipLaunchKernelGGL(route_count_kernel, dim3(nblk), dim3(kBlockThreads), 0, stream, ids, R, E,
+                       scratch);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(route_place_kernel, dim3(nblk), dim3(kBlockThreads), 0, stream, ids, R, k, E,
+                       nblk, scratch, counts, offsets, slot_row, row_token);
     return hipGetLastError();
 }
 
