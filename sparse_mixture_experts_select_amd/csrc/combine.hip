@@ -16,6 +16,8 @@
 namespace moe {
 namespace {
 
+constexpr int kMaxPicks = 8;  // k <= 8 (checked by the entry points)
+
 template <typename T> struct Io;
 template <> struct Io<bf16> {
     __device__ static void load4(const void* p, size_t i, float* v) {
@@ -39,6 +41,11 @@ template <> struct Io<float> {
     }
 };
 
+// One token per workgroup iteration; each thread takes 4 float4 columns
+// (256 apart) of every pick at once, so all of a token's loads are in flight
+// together.  Per column the sum order is fixed: for each pick j = 0..k-1 in
+// slot order, its K slices s = 0..splits-1 summed first, then g_j times that
+// added to the running sum.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int splits,
                                                       size_t split_stride,
@@ -46,29 +53,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ slot_row,
                                                       const void* residual, int Tn, int d, int k,
                                                       void* out) {
+    constexpr int U = 4;
     const int d4 = d / 4;
     for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
-        for (int c = threadIdx.x; c < d4; c += 256) {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int j = 0; j < k; ++j) {
-                const int r = slot_row[(size_t)t * k + j];
-                const float g = gates[(size_t)t * k + j];
-                const float4* yr = reinterpret_cast<const float4*>(y + (size_t)r * d);
-                float4 s = yr[c];
-                for (int p = 1; p < splits; ++p) {
-                    const float4 v =
-                        reinterpret_cast<const float4*>(y + p * split_stride + (size_t)r * d)[c];
-                    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        int rows[kMaxPicks];
+        float g[kMaxPicks];
+#pragma unroll
+        for (int j = 0; j < kMaxPicks; ++j) {
+            rows[j] = j < k ? slot_row[(size_t)t * k + j] : 0;
+            g[j] = j < k ? gates[(size_t)t * k + j] : 0.0f;
+        }
+        for (int c0 = threadIdx.x; c0 < d4; c0 += 256 * U) {
+            float4 acc[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < kMaxPicks; ++j) {
+                if (j >= k) break;
+                const float4* yr = reinterpret_cast<const float4*>(y + (size_t)rows[j] * d);
+                float4 sv[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + 256 * u;
+                    sv[u] = c < d4 ? yr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
                 }
-                acc[0] += g * s.x; acc[1] += g * s.y; acc[2] += g * s.z; acc[3] += g * s.w;
+                for (int p = 1; p < splits; ++p) {
+                    const float4* yp = reinterpret_cast<const float4*>(y + p * split_stride + (size_t)rows[j] * d);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int c = c0 + 256 * u;
+                        if (c < d4) {
+                            const float4 v = yp[c];
+                            sv[u].x += v.x; sv[u].y += v.y; sv[u].z += v.z; sv[u].w += v.w;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    acc[u].x += g[j] * sv[u].x; acc[u].y += g[j] * sv[u].y;
+                    acc[u].z += g[j] * sv[u].z; acc[u].w += g[j] * sv[u].w;
+                }
             }
-            const size_t idx = (size_t)t * d4 + c;
-            if (residual != nullptr) {
-                float rv[4];
-                Io<T>::load4(residual, idx, rv);
-                for (int u = 0; u < 4; ++u) acc[u] = rv[u] + acc[u];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + 256 * u;
+                if (c >= d4) continue;
+                const size_t idx = (size_t)t * d4 + c;
+                float a[4] = {acc[u].x, acc[u].y, acc[u].z, acc[u].w};
+                if (residual != nullptr) {
+                    float rv[4];
+                    Io<T>::load4(residual, idx, rv);
+                    for (int q = 0; q < 4; ++q) a[q] = rv[q] + a[q];
+                }
+                Io<T>::store4(out, idx, a);
             }
-            Io<T>::store4(out, idx, acc);
         }
     }
 }
