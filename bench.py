@@ -50,6 +50,12 @@ CALIBRATION_BYTES = 1 << 30
 PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d gpurun_out/pmc_{tag} -o run -- "
                "python3 bench.py --steps 3 --warmup 1 --stack off --skewed off --no-cpu-baseline "
                "--calibrate-copy")
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE GRBM_COUNT"
+MFMA_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv "
+                "-d gpurun_out/pmc_mfma -o run -- python3 bench.py --workload prefill --secondary none "
+                "--steps 3 --warmup 1 --stack off --skewed off --no-cpu-baseline")
+SIMDS = 256 * 4          # MI355X: 256 CUs x 4 SIMDs
+NOMINAL_CLOCK_HZ = 2.4e9  # the clock the 2.5 PFLOP/s figure assumes
 TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o run -- "
                  "python3 bench.py --steps 10 --warmup 2 --cpu-seconds 2")
 
@@ -367,8 +373,22 @@ def cpu_baseline(res, seconds, inputs):
         if el >= seconds or reps >= 50:
             break
     tok_s = reps * n_tok / el
+    cpu_model, ram_gb = "unknown", None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as fh:
+            for line in fh:
+                if line.startswith("MemTotal"):
+                    ram_gb = round(int(line.split()[1]) / 1024 ** 2, 1)
+                    break
+    except OSError:
+        pass
     return {"value": round(tok_s, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "ram_gb": ram_gb, "nproc": os.cpu_count(),
             "sample": "%s workload, tokens 0..%d (full layer per token in fp64), %d passes, %.1f s"
                       % (wl.name, n_tok - 1, reps, el)}
 
@@ -445,6 +465,65 @@ def summarize_counters(fetch_dir, write_dir):
         log("[bench] wrote", out)
     if not written:
         raise SystemExit("no w1/w3 kernel dispatches found")
+
+
+def summarize_mfma(run_dir):
+    """Turn one rocprofv3 --pmc run of MFMA_COMMAND into
+    profiles/gemm1_swiglu_prefill_mfma.txt: per launch of the prefill w1/w3
+    kernel its MFMA busy cycles (summed over all SIMDs), the bf16 MFMA work it
+    issued (SQ_INSTS_VALU_MFMA_MOPS_BF16, units of 512 flops) against the
+    algorithmic 4 T k d f, and the MFMA busy fraction over the dispatch's own
+    duration at the nominal clock."""
+    import re
+    import statistics
+
+    rows = _counter_rows(run_dir)
+    pattern = GEMM1_KERNEL["prefill"][1]
+    per = {}
+    span = {}
+    for r in rows:
+        if not re.search(pattern, r["Kernel_Name"]):
+            continue
+        per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        span[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    if len(per) < 4 or not span:
+        raise SystemExit("no prefill w1/w3 dispatches with all counters in %s" % run_dir)
+    avg = {k: statistics.mean(v) for k, v in per.items()}
+    dur = statistics.mean(span.values())
+    from sparse_mixture_experts_select_amd import inputs
+    wl = inputs.WORKLOADS["prefill"]
+    alg_flops = 4.0 * wl.T * wl.k * wl.d * wl.f
+    issued_flops = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+    busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"]
+    out = os.path.join(ROOT, "profiles", "gemm1_swiglu_prefill_mfma.txt")
+    with open(out, "w") as fh:
+        fh.write("# MFMA use of the w1/w3 grouped GEMM + SwiGLU kernel, prefill workload "
+                 "(T=4096, d=4096, f=14336, E=8, k=2, bf16)\n")
+        fh.write("# kernel: %s (source %s)\n" % (pattern, GEMM1_KERNEL["prefill"][0]))
+        fh.write("# command: %s\n" % MFMA_COMMAND)
+        fh.write("# summarized by: python3 bench.py --summarize-mfma gpurun_out/pmc_mfma\n")
+        fh.write("# counters per launch (averages over %d launches); SQ_VALU_MFMA_BUSY_CYCLES is "
+                 "summed over all %d SIMDs (a 16x16x32 bf16 MFMA keeps its SIMD busy 16 cycles)\n"
+                 % (len(span), SIMDS))
+        for k in sorted(avg):
+            fh.write("%s = %.0f\n" % (k, avg[k]))
+        fh.write("dispatch_seconds = %.6e\n" % dur)
+        fh.write("algorithmic_flops = %.6e\n" % alg_flops)
+        fh.write("issued_mfma_flops = %.6e\n" % issued_flops)
+        fh.write("issued_over_algorithmic = %.4f  (rows of partial tiles computed and not stored)\n"
+                 % (issued_flops / alg_flops))
+        fh.write("mfma_busy_cycles_per_simd = %.0f\n" % (busy / SIMDS))
+        fh.write("mfma_busy_fraction_at_2.4GHz = %.4f  (busy cycles / (SIMDs x duration x 2.4 GHz))\n"
+                 % (busy / (SIMDS * dur * NOMINAL_CLOCK_HZ)))
+        # GRBM_GUI_ACTIVE counts the cycles the GPU is busy, summed over its 8
+        # XCDs, at the clock it actually runs (cross-checked against a kernel
+        # probe of s_memtime against the 100 MHz real-time counter)
+        clock = avg["GRBM_GUI_ACTIVE"] / 8 / dur
+        fh.write("clock_ghz_from_grbm = %.3f  (GRBM_GUI_ACTIVE / 8 XCDs / duration)\n" % (clock / 1e9))
+        fh.write("mfma_busy_fraction_at_that_clock = %.4f\n" % (busy / (SIMDS * dur * clock)))
+        fh.write("achieved_tflops_in_dispatch = %.1f\n" % (alg_flops / dur / 1e12))
+        fh.write("bf16_peak_at_that_clock_tflops = %.1f\n" % (SIMDS * 1024 * clock / 1e12))
+    log("[bench] wrote", out)
 
 
 def _short_kernel_name(name):
@@ -530,11 +609,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     args = ap.parse_args()
 
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
@@ -578,6 +661,8 @@ def main():
                   "hbm_frac": round(prim["layer_gbs"] / HBM_PEAK_GBS, 4)},
         "stages_ms": prim["stage_ms"],
         "step_ms": prim["step_ms"],
+        "note": ("each step streams the expert weights from HBM: one layer's 2.82 GB exceeds the "
+                 "256 MiB MALL, so no cache flush is needed between steps"),
     }
     def side_workload(name):
         # free the primary inputs while another workload runs
