@@ -195,13 +195,13 @@ def run_workload(name, steps, warmup, binding, inputs, torch):
 def run_stack(steps, warmup, binding, inputs, torch):
     """The 32-block stack h <- h + MoE(RMSNorm(h)) at T=2048 with all layers'
     weights resident.  A step restores h0 (one 16 MiB copy) and runs the 32
-    blocks (RMSNorm + layer with the residual added in the combine)."""
+    blocks, one library call each (the router forms RMSNorm(h), the combine
+    adds the residual in place)."""
     wl = inputs.WORKLOADS["stack"]
     layers = [inputs.make_weights(wl.d, wl.f, wl.E, torch.bfloat16, "cuda", 0, "stack", layer)
               for layer in range(wl.layers)]
     h0 = inputs.make_x(wl.T, wl.d, torch.bfloat16, "cuda", wl.x_dist, 0, "stack")
     h = torch.empty_like(h0)
-    x = torch.empty_like(h0)
     counts = [torch.zeros(wl.E, dtype=torch.int32, device="cuda") for _ in layers]
     torch.cuda.synchronize()
     log("[bench] stack: %d layers resident (%.1f GB of expert weights)"
@@ -210,9 +210,8 @@ def run_stack(steps, warmup, binding, inputs, torch):
     def step(with_counts=False):
         h.copy_(h0)
         for i, w in enumerate(layers):
-            binding.moe_rmsnorm(h, x, eps=wl.rms_eps)
-            binding.moe_ffn_forward_ex(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=h,
-                                       residual=h,
+            binding.moe_ffn_forward_ex(h, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=h,
+                                       residual=h, rmsnorm_eps=wl.rms_eps,
                                        expert_counts=counts[i] if with_counts else None)
 
     step(with_counts=True)
@@ -259,9 +258,8 @@ def run_stack(steps, warmup, binding, inputs, torch):
     def step_ws():
         h.copy_(h0)
         for w in layers:
-            binding.moe_rmsnorm(h, x, eps=wl.rms_eps)
-            binding.moe_ffn_forward_ex(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=h,
-                                       residual=h, workspace=ws)
+            binding.moe_ffn_forward_ex(h, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=h,
+                                       residual=h, rmsnorm_eps=wl.rms_eps, workspace=ws)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -391,6 +389,31 @@ def cpu_baseline(res, seconds, inputs):
             "kind": "oracle", "cpu_model": cpu_model, "ram_gb": ram_gb, "nproc": os.cpu_count(),
             "sample": "%s workload, tokens 0..%d (full layer per token in fp64), %d passes, %.1f s"
                       % (wl.name, n_tok - 1, reps, el)}
+
+
+def read_probe(torch, binding, nbytes=4 << 30, reps=3):
+    """Measured streaming-read rate of this GPU: the library's read probe
+    (16-byte loads in a grid-stride loop) over a buffer far larger than the
+    256 MiB MALL, best over a few grid sizes and `reps` timed passes each."""
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = None
+    for blocks in (256, 384, 512, 768, 1024, 2048, 4096):
+        binding.moe_hbm_read_probe(buf, blocks, sink)
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            binding.moe_hbm_read_probe(buf, blocks, sink)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            if best is None or ms < best[0]:
+                best = (ms, blocks)
+    del buf
+    torch.cuda.empty_cache()
+    gbs = nbytes / (best[0] * 1e-3) / 1e9
+    log("[bench] read probe: %.1f GB/s (%d bytes, %d workgroups)" % (gbs, nbytes, best[1]))
+    return gbs, best[1]
 
 
 def calibrate_copy(torch, nbytes=CALIBRATION_BYTES, reps=3):
@@ -576,8 +599,8 @@ def summarize_trace(trace_dir):
     out = os.path.join(ROOT, "profiles", "moe_layer_decode_prefill_stack_kernel_stats.txt")
     with open(out, "w") as fh:
         fh.write("# rocprofv3 kernel trace of the benchmark: decode (T=32), prefill (T=4096), "
-                 "skewed routing (T=16384), then the 32-block stack (T=2048; rmsnorm + layer per "
-                 "block); d=4096 f=14336 E=8 k=2 bf16\n")
+                 "skewed routing (T=16384), then the 32-block stack (T=2048; one layer call per "
+                 "block, RMSNorm formed by the router); d=4096 f=14336 E=8 k=2 bf16\n")
         fh.write("# command: %s\n" % TRACE_COMMAND)
         fh.write("# summarized by: python3 bench.py --summarize-trace gpurun_out/trace\n")
         fh.write("# calls = warm-up + one routing probe call + timed steps; durations in us; "
@@ -707,6 +730,15 @@ def main():
         prim["inp"] = inputs.workload_inputs(args.workload, "cuda")
     if args.calibrate_copy:
         calibrate_copy(torch)
+    if bound == "hbm":
+        probe, blocks = read_probe(torch, binding)
+        rec["read_probe"] = {
+            "what": "streaming read of a 4 GiB buffer, 16-byte loads, %d workgroups of 256 "
+                    "(moe_hbm_read_probe)" % blocks,
+            "gbs": round(probe, 1),
+            "gemm1_frac_of_probe": round(rec["roofline"]["achieved"] / probe, 4),
+            "layer_frac_of_probe": round(prim["layer_gbs"] / probe, 4),
+        }
     if args.no_cpu_baseline:
         rec["cpu_baseline"] = None
     else:

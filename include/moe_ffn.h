@@ -96,6 +96,17 @@ moe_status_t moe_ffn_forward_f32(const float *x, const float *w_router, const fl
  *                  formed in fp32 and rounded once.  residual == out is allowed.
  *   workspace      caller-owned device scratch of workspace_bytes bytes, at
  *                  least moe_ffn_workspace_bytes(...); NULL = library cache.
+ *   rmsnorm_input  nonzero: x holds the residual stream h of the stacked
+ *                  block h = h + MoE(RMSNorm(h)), and the layer runs on
+ *                  RMSNorm(h) with unit gain and eps = rmsnorm_eps (>= 0,
+ *                  finite), formed by the router while it reads h, with the
+ *                  same bits as moe_rmsnorm.  The pages leave normalisation
+ *                  details to the code ("Method", steps for one token, item 5).
+ *                  With residual == out == x, one call is one whole block.
+ *   rmsnorm_eps    see rmsnorm_input.
+ *   x_norm_out     [T,d] out (dtype), used only with rmsnorm_input: receives
+ *                  RMSNorm(h).  Must not overlap x, out or residual.  NULL =
+ *                  kept in the workspace.
  */
 typedef struct moe_ffn_opts {
     int32_t dtype;
@@ -111,6 +122,9 @@ typedef struct moe_ffn_opts {
     const void *residual;
     void *workspace;
     size_t workspace_bytes;
+    int32_t rmsnorm_input;
+    float rmsnorm_eps;
+    void *x_norm_out;
 } moe_ffn_opts_t;
 
 /* The layer with options; opts == NULL behaves as moe_ffn_forward. */
@@ -156,6 +170,19 @@ moe_status_t moe_rmsnorm(const void *h, void *x, int64_t T, int64_t d, float eps
 moe_status_t moe_ffn_profile_begin(int32_t max_calls, uint32_t stage_mask);
 moe_status_t moe_ffn_profile_end(float *stage_ms, int32_t *calls);
 const char *moe_ffn_stage_name(int32_t stage);
+
+/*
+ * Measurement aid, not part of the layer: a plain streaming read of `bytes`
+ * bytes of device memory at buf (16-byte aligned, bytes a multiple of 16) by
+ * `blocks` workgroups of 256 threads (1..65536), each reading 16-byte vectors
+ * in a grid-stride loop.  *sink (a device uint32) receives an XOR fold of the
+ * data, which only keeps the loads live.  Timing it over a buffer far larger
+ * than the 256 MiB MALL gives the read rate a streaming kernel can reach on
+ * this GPU, the measured ceiling beside the 8 TB/s datasheet figure.
+ * Enqueued on `stream`; bytes == 0 is a no-op.
+ */
+moe_status_t moe_hbm_read_probe(const void *buf, size_t bytes, int32_t blocks, uint32_t *sink,
+                                void *stream);
 
 /* Text describing the last non-OK status returned on this host thread. */
 const char *moe_ffn_last_error(void);

@@ -54,6 +54,9 @@ class MoeFfnOpts(ctypes.Structure):
         ("residual", _P),
         ("workspace", _P),
         ("workspace_bytes", ctypes.c_size_t),
+        ("rmsnorm_input", ctypes.c_int32),
+        ("rmsnorm_eps", ctypes.c_float),
+        ("x_norm_out", _P),
     ]
 
 
@@ -80,6 +83,8 @@ lib.moe_ffn_stage_name.argtypes = [ctypes.c_int32]
 lib.moe_ffn_stage_name.restype = ctypes.c_char_p
 lib.moe_ffn_version.argtypes = []
 lib.moe_ffn_version.restype = ctypes.c_char_p
+lib.moe_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, ctypes.c_int32, _P, _P]
+lib.moe_hbm_read_probe.restype = ctypes.c_int
 
 
 class MoeError(RuntimeError):
@@ -154,9 +159,11 @@ def moe_ffn_forward_f32(x, w_router, w1, w3, w2, k, out=None, stream=None):
 def moe_ffn_forward_ex(x, w_router, w1, w3, w2, k, out=None, stream=None, *, router_bias=None,
                        topk_ids=None, topk_weights=None, expert_counts=None, expert_offsets=None,
                        row_token=None, slot_row=None, h_out=None, y_out=None, residual=None,
-                       workspace=None):
-    """The layer with options (see ``moe_ffn_opts_t``); every option is a GPU
-    tensor or None.  Returns ``out``."""
+                       workspace=None, rmsnorm_eps=None, x_norm_out=None):
+    """The layer with options (see ``moe_ffn_opts_t``); every tensor option is
+    a GPU tensor or None.  ``rmsnorm_eps`` set: x is the residual stream h and
+    the layer runs on RMSNorm(h) (formed by the router; ``x_norm_out``, if
+    given, receives it).  Returns ``out``."""
     T, d, f, E = _shapes(x, w_router, w1, w3, w2)
     if out is None:
         out = torch.empty_like(x)
@@ -171,7 +178,10 @@ def moe_ffn_forward_ex(x, w_router, w1, w3, w2, k, out=None, stream=None, *, rou
         "expert_offsets": (expert_offsets, E + 1, i32), "row_token": (row_token, R, i32),
         "slot_row": (slot_row, R, i32), "h_out": (h_out, R * f, x.dtype),
         "y_out": (y_out, R * d, f32), "residual": (residual, T * d, x.dtype),
+        "x_norm_out": (x_norm_out, T * d, x.dtype),
     }
+    if x_norm_out is not None and rmsnorm_eps is None:
+        raise ValueError("x_norm_out needs rmsnorm_eps")
     opts = MoeFfnOpts()
     opts.dtype = _dtype_code(x.dtype)
     for name, (t, n, dt) in spec.items():
@@ -186,6 +196,9 @@ def moe_ffn_forward_ex(x, w_router, w1, w3, w2, k, out=None, stream=None, *, rou
     if workspace is not None:
         opts.workspace = workspace.data_ptr()
         opts.workspace_bytes = workspace.numel() * workspace.element_size()
+    if rmsnorm_eps is not None:
+        opts.rmsnorm_input = 1
+        opts.rmsnorm_eps = float(rmsnorm_eps)
     _check(lib.moe_ffn_forward_ex(_ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3), _ptr(w2),
                                   T, d, f, E, k, _ptr(out), _stream(stream), ctypes.byref(opts)))
     return out
@@ -204,6 +217,15 @@ def moe_rmsnorm(h, x=None, eps=1e-5, stream=None):
     T, d = h.shape
     _check(lib.moe_rmsnorm(_ptr(h), _ptr(x), T, d, float(eps), _dtype_code(h.dtype), _stream(stream)))
     return x
+
+
+def moe_hbm_read_probe(buf, blocks, sink, stream=None) -> None:
+    """Enqueue one streaming read of the whole GPU tensor ``buf`` (see the
+    header); ``sink`` is a one-element int32 GPU tensor."""
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda or sink.dtype != torch.int32:
+        raise ValueError("buf must be a contiguous GPU tensor and sink an int32 GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.moe_hbm_read_probe(_ptr(buf), nbytes, int(blocks), _ptr(sink), _stream(stream)))
 
 
 def moe_ffn_last_error() -> str:

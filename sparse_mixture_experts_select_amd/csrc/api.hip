@@ -236,13 +236,23 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     if (T == 0) return MOE_OK;
     if (!x || !w_router || !w1 || !w3 || !w2 || !out)
         return fail(MOE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+    const bool norm_in = opts && opts->rmsnorm_input != 0;
     const void* must_align[] = {x, w_router, w1, w3, w2, out,
                                 opts ? opts->residual : nullptr,
                                 opts ? opts->h_out : nullptr,
                                 opts ? (const void*)opts->y_out : nullptr,
-                                opts ? opts->workspace : nullptr};
+                                opts ? opts->workspace : nullptr,
+                                norm_in ? opts->x_norm_out : nullptr};
     for (const void* p : must_align)
         if (p && !aligned16(p)) return fail(MOE_ERR_UNSUPPORTED, "a tensor pointer is not 16-byte aligned");
+    if (norm_in) {
+        const float eps = opts->rmsnorm_eps;
+        if (!(eps >= 0.0f) || eps > 3.0e38f)
+            return fail(MOE_ERR_INVALID_ARG, "rmsnorm_eps must be finite and >= 0");
+        const void* xn = opts->x_norm_out;
+        if (xn && (xn == x || xn == out || xn == opts->residual))
+            return fail(MOE_ERR_INVALID_ARG, "x_norm_out must not overlap x, out or residual");
+    }
 
     const Plan plan = make_plan(T, d, f, E, k, dtype);
     char* ws = nullptr;
@@ -284,8 +294,17 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     auto skip = [&](int s) {
         if (ev) *prof_skipped |= 1u << s;
     };
+    // With rmsnorm_input the router writes x = RMSNorm(h) and the later
+    // steps read that.  Without x_norm_out it goes to the y region, which is
+    // free until GEMM 2 (by then every reader of x has run) and holds at
+    // least T*d fp32 values.
+    void* x_norm = nullptr;
+    if (norm_in) x_norm = opts->x_norm_out ? opts->x_norm_out : (void*)y;
     mark(0);
-    LAUNCH(launch_router_topk(dtype, x, w_router, bias, Ti, di, Ei, ki, ids, gates, stream), "router_topk");
+    LAUNCH(launch_router_topk(dtype, x, w_router, bias, Ti, di, Ei, ki, ids, gates, x_norm,
+                              norm_in ? opts->rmsnorm_eps : 0.0f, stream),
+           "router_topk");
+    if (norm_in) x = x_norm;
     mark(1);
     LAUNCH(launch_route_scan(ids, Ti, ki, Ei, counts, offsets, slot_row, row_token,
                              reinterpret_cast<int32_t*>(ws + plan.scan), stream),
@@ -460,6 +479,18 @@ void moe_ffn_release_workspace(void) {
         c.bytes = 0;
     }
     if (have_cur) (void)hipSetDevice(cur);
+}
+
+moe_status_t moe_hbm_read_probe(const void* buf, size_t bytes, int32_t blocks, uint32_t* sink,
+                                void* stream) {
+    if (bytes == 0) return MOE_OK;
+    if (!buf || !sink) return fail(MOE_ERR_INVALID_ARG, "a pointer is NULL");
+    if (!aligned16(buf) || bytes % 16 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "buf must be 16-byte aligned and bytes a multiple of 16");
+    if (blocks < 1 || blocks > 65536) return fail(MOE_ERR_INVALID_ARG, "blocks must be in [1, 65536]");
+    LAUNCH(launch_read_probe(buf, bytes, blocks, sink, reinterpret_cast<hipStream_t>(stream)),
+           "read_probe");
+    return MOE_OK;
 }
 
 const char* moe_ffn_version(void) { return "0.1.0"; }

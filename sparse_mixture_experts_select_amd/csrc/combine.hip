@@ -10,7 +10,9 @@
 //
 // RMSNorm (unit gain) serves the stacked form h = h + MoE(RMSNorm(h)); the
 // pages leave the normalisation to the code ("Method", steps for one token,
-// item 5).  One workgroup per row, fp32 sum of squares, one rounding.
+// item 5).  One workgroup per row, fp32 sum of squares, one rounding.  The
+// router's fused form (router.hip) accumulates in exactly this order, so the
+// two give the same bits.
 #include "common.h"
 
 namespace moe {
@@ -39,6 +41,26 @@ template <> struct Io<float> {
     __device__ static void store4(void* p, size_t i, const float* v) {
         reinterpret_cast<float4*>(p)[i] = make_float4(v[0], v[1], v[2], v[3]);
     }
+};
+
+// 16-byte slices: 8 bf16 or 4 fp32 elements.
+template <typename T> struct Io16;
+template <> struct Io16<bf16> {
+    static constexpr int N = 8;
+    __device__ static void load(const void* p, size_t i, float* v) {
+        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    }
+    __device__ static void store(void* p, size_t i, const float* v) {
+        reinterpret_cast<uint4*>(p)[i] = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    }
+};
+template <> struct Io16<float> {
+    static constexpr int N = 4;
+    __device__ static void load(const void* p, size_t i, float* v) { Io<float>::load4(p, i, v); }
+    __device__ static void store(void* p, size_t i, const float* v) { Io<float>::store4(p, i, v); }
 };
 
 // One token per workgroup iteration; each thread takes 4 float4 columns
@@ -115,24 +137,26 @@ template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* h, void* x, int Tn, int d,
                                                       float eps) {
     __shared__ float part[4];
-    const int d4 = d / 4;
+    constexpr int N = Io16<T>::N;
+    const int ds = d / N;  // 16-byte slices per row
     for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
         float ss = 0.0f;
-        for (int c = threadIdx.x; c < d4; c += 256) {
-            float v[4];
-            Io<T>::load4(h, (size_t)t * d4 + c, v);
-            ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+        for (int c = threadIdx.x; c < ds; c += 256) {
+            float v[N];
+            Io16<T>::load(h, (size_t)t * ds + c, v);
+#pragma unroll
+            for (int u = 0; u < N; ++u) ss = fmaf(v[u], v[u], ss);
         }
         for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
         if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
         __syncthreads();
-        const float tot = part[0] + part[1] + part[2] + part[3];
-        const float r = 1.0f / sqrtf(tot / (float)d + eps);
-        for (int c = threadIdx.x; c < d4; c += 256) {
-            float v[4];
-            Io<T>::load4(h, (size_t)t * d4 + c, v);
-            for (int u = 0; u < 4; ++u) v[u] *= r;
-            Io<T>::store4(x, (size_t)t * d4 + c, v);
+        const float r = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
+        for (int c = threadIdx.x; c < ds; c += 256) {
+            float v[N];
+            Io16<T>::load(h, (size_t)t * ds + c, v);
+#pragma unroll
+            for (int u = 0; u < N; ++u) v[u] *= r;
+            Io16<T>::store(x, (size_t)t * ds + c, v);
         }
         __syncthreads();
     }

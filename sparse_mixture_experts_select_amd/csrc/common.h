@@ -31,9 +31,11 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-
 // Kernel launchers.  Each returns the hipGetLastError() of its launch(es).
 // dtype: 0 = bf16, 1 = fp32 (same codes as moe_dtype_t).
 
+// xn: when non-null, x holds h and the router writes x = RMSNorm(h) (eps,
+// unit gain, the same bits as launch_rmsnorm) to xn and routes that.
 hipError_t launch_router_topk(int dtype, const void* x, const void* w_router, const float* bias,
-                              int T, int d, int E, int k, int32_t* ids, float* gates,
-                              hipStream_t stream);
+                              int T, int d, int E, int k, int32_t* ids, float* gates, void* xn,
+                              float eps, hipStream_t stream);
 
 // scratch: route_scan_scratch_bytes(T * k, E) bytes (0: may be null)
 size_t route_scan_scratch_bytes(int R, int E);
@@ -98,6 +100,10 @@ hipError_t launch_sum_splits(const float* y, int splits, int R, int d, float* y_
 
 hipError_t launch_rmsnorm(int dtype, const void* h, void* x, int T, int d, float eps,
                           hipStream_t stream);
+
+// Streaming read of `bytes` (a multiple of 16) from buf; XOR fold to *sink.
+hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink,
+                             hipStream_t stream);
 
 // Tile shapes of the bf16 grouped GEMMs, chosen by the host per call.
 enum GemmVariant { GEMM_LARGE_M = 0, GEMM_SMALL_M = 1, GEMM_STREAM = 2, GEMM_TILE256 = 3 };

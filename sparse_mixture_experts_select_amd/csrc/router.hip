@@ -20,6 +20,15 @@
 // Logits stay fp32 (products of bf16 inputs are exact in fp32, sums are
 // fp32).  Ties break toward the lower expert index; the picks are stored by
 // descending logit.  An optional fp32 bias [E] is added before selection.
+//
+// Fused RMSNorm (NORM): the input rows are the residual stream h of the
+// stacked block h = h + MoE(RMSNorm(h)).  A first pass over the row forms
+// its sum of squares, the second scales each 16-byte slice by
+// 1/sqrt(mean + eps), rounds it once to the storage type, stores it as the
+// layer input x, and takes the logits from those rounded values.  The sum of
+// squares is accumulated in the same order as rmsnorm_kernel (the same
+// slices per thread, fmaf in element order, a butterfly over the wave, the
+// four waves in order), so both forms give x bit for bit.
 #include "common.h"
 
 namespace moe {
@@ -38,6 +47,17 @@ template <> struct Vec<bf16> {
         v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     }
     __device__ static float one(const bf16* p, size_t i) { return (float)p[i]; }
+    // v <- round(v * r), stored to p; v keeps the rounded values.
+    __device__ static void scale_store(float* v, float r, bf16* p) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            w[q] = pack_bf16x2(v[2 * q] * r, v[2 * q + 1] * r);
+            v[2 * q] = bf16_lo(w[q]);
+            v[2 * q + 1] = bf16_hi(w[q]);
+        }
+        *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
 };
 template <> struct Vec<float> {
     static constexpr int N = 4;
@@ -46,6 +66,11 @@ template <> struct Vec<float> {
         v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
     }
     __device__ static float one(const float* p, size_t i) { return p[i]; }
+    __device__ static void scale_store(float* v, float r, float* p) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] *= r;
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
 };
 
 template <int NV>
@@ -83,15 +108,45 @@ __device__ __forceinline__ void wave_sum_split(float (&v)[NV], int lane) {
 }
 
 // ROWS8: bf16 router rows of exactly 8 experts, read as one 16-byte vector.
-template <typename T, int EMAX, int TPW, bool ROWS8>
+// NORM: x holds h; RMSNorm(h) (eps) is written to xn and routed.
+template <typename T, int EMAX, int TPW, bool ROWS8, bool NORM>
 __global__ __launch_bounds__(kThreads) void router_topk_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ bias, int T_,
-    int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ gates) {
+    int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ gates, T* __restrict__ xn,
+    float eps) {
     __shared__ float part[kWaves][TPW][EMAX];
+    __shared__ float sumsq[NORM ? kWaves : 1][TPW];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     constexpr int VN = Vec<T>::N;
     const int t0 = blockIdx.x * TPW;
+
+    // RMSNorm scale of each token (NORM only).
+    float rs[TPW];
+    if constexpr (NORM) {
+        float ss[TPW];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) ss[tt] = 0.0f;
+        for (int i0 = threadIdx.x * VN; i0 < d; i0 += kThreads * VN) {
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                if (t0 + tt < T_) {
+                    float v[VN];
+                    Vec<T>::load(x + (size_t)(t0 + tt) * d + i0, v);
+#pragma unroll
+                    for (int u = 0; u < VN; ++u) ss[tt] = fmaf(v[u], v[u], ss[tt]);
+                }
+            }
+        }
+        constexpr int SH = 6 - log2_of<TPW>();
+        wave_sum_split<TPW>(ss, lane);
+        if ((lane & ((1 << SH) - 1)) == 0) sumsq[wave][lane >> SH] = ss[0];
+        __syncthreads();
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+            rs[tt] = 1.0f / sqrtf((sumsq[0][tt] + sumsq[1][tt] + sumsq[2][tt] + sumsq[3][tt]) /
+                                      (float)d + eps);
+    }
 
     float acc[TPW][EMAX];
 #pragma unroll
@@ -105,6 +160,7 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
         for (int tt = 0; tt < TPW; ++tt) {
             if (t0 + tt < T_) {
                 Vec<T>::load(x + (size_t)(t0 + tt) * d + i0, xv[tt]);
+                if constexpr (NORM) Vec<T>::scale_store(xv[tt], rs[tt], xn + (size_t)(t0 + tt) * d + i0);
             } else {
 #pragma unroll
                 for (int u = 0; u < VN; ++u) xv[tt][u] = 0.0f;
@@ -206,45 +262,52 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
 
 template <typename T, int EMAX, int TPW, bool ROWS8>
 hipError_t launch_t(const void* x, const void* wr, const float* bias, int T_, int d, int E, int k,
-                    int32_t* ids, float* gates, hipStream_t stream) {
+                    int32_t* ids, float* gates, void* xn, float eps, hipStream_t stream) {
     const int blocks = (T_ + TPW - 1) / TPW;
-    hipLaunchKernelGGL((router_topk_kernel<T, EMAX, TPW, ROWS8>), dim3(blocks), dim3(kThreads), 0,
-                       stream, reinterpret_cast<const T*>(x), reinterpret_cast<const T*>(wr), bias,
-                       T_, d, E, k, ids, gates);
+    if (xn != nullptr)
+        hipLaunchKernelGGL((router_topk_kernel<T, EMAX, TPW, ROWS8, true>), dim3(blocks),
+                           dim3(kThreads), 0, stream, reinterpret_cast<const T*>(x),
+                           reinterpret_cast<const T*>(wr), bias, T_, d, E, k, ids, gates,
+                           reinterpret_cast<T*>(xn), eps);
+    else
+        hipLaunchKernelGGL((router_topk_kernel<T, EMAX, TPW, ROWS8, false>), dim3(blocks),
+                           dim3(kThreads), 0, stream, reinterpret_cast<const T*>(x),
+                           reinterpret_cast<const T*>(wr), bias, T_, d, E, k, ids, gates,
+                           static_cast<T*>(nullptr), 0.0f);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t dispatch_e(const void* x, const void* wr, const float* bias, int T_, int d, int E,
-                      int k, int32_t* ids, float* gates, hipStream_t stream) {
+                      int k, int32_t* ids, float* gates, void* xn, float eps, hipStream_t stream) {
     // Larger batches share each router row load among more tokens of a
     // workgroup (measured on MI355X at d = 4096: 1 token per workgroup is
     // fastest up to a few hundred tokens, 8 from a few thousand).
     const bool big = T_ > 1024;
     if constexpr (sizeof(T) == 2) {
         if (E == 8) {
-            if (T_ > 2048) return launch_t<T, 8, 8, true>(x, wr, bias, T_, d, E, k, ids, gates, stream);
-            if (T_ > 768) return launch_t<T, 8, 4, true>(x, wr, bias, T_, d, E, k, ids, gates, stream);
-            if (T_ > 384) return launch_t<T, 8, 2, true>(x, wr, bias, T_, d, E, k, ids, gates, stream);
-            return launch_t<T, 8, 1, true>(x, wr, bias, T_, d, E, k, ids, gates, stream);
+            if (T_ > 2048) return launch_t<T, 8, 8, true>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
+            if (T_ > 768) return launch_t<T, 8, 4, true>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
+            if (T_ > 384) return launch_t<T, 8, 2, true>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
+            return launch_t<T, 8, 1, true>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
         }
     }
     if (E <= 8) {
-        if (big) return launch_t<T, 8, 4, false>(x, wr, bias, T_, d, E, k, ids, gates, stream);
-        return launch_t<T, 8, 1, false>(x, wr, bias, T_, d, E, k, ids, gates, stream);
+        if (big) return launch_t<T, 8, 4, false>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
+        return launch_t<T, 8, 1, false>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
     }
-    if (E <= 16) return launch_t<T, 16, 2, false>(x, wr, bias, T_, d, E, k, ids, gates, stream);
-    if (E <= 32) return launch_t<T, 32, 1, false>(x, wr, bias, T_, d, E, k, ids, gates, stream);
-    return launch_t<T, 64, 1, false>(x, wr, bias, T_, d, E, k, ids, gates, stream);
+    if (E <= 16) return launch_t<T, 16, 2, false>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
+    if (E <= 32) return launch_t<T, 32, 1, false>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
+    return launch_t<T, 64, 1, false>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
 }
 
 }  // namespace
 
 hipError_t launch_router_topk(int dtype, const void* x, const void* w_router, const float* bias,
-                              int T, int d, int E, int k, int32_t* ids, float* gates,
-                              hipStream_t stream) {
-    if (dtype == 0) return dispatch_e<bf16>(x, w_router, bias, T, d, E, k, ids, gates, stream);
-    return dispatch_e<float>(x, w_router, bias, T, d, E, k, ids, gates, stream);
+                              int T, int d, int E, int k, int32_t* ids, float* gates, void* xn,
+                              float eps, hipStream_t stream) {
+    if (dtype == 0) return dispatch_e<bf16>(x, w_router, bias, T, d, E, k, ids, gates, xn, eps, stream);
+    return dispatch_e<float>(x, w_router, bias, T, d, E, k, ids, gates, xn, eps, stream);
 }
 
 }  // namespace moe

@@ -24,8 +24,9 @@ GAP = 1e-3
 TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
 
 
-def run_gpu(inp, k, want_h=False, want_y=False, residual=None):
-    """One forward through moe_ffn_forward_ex with every debug output."""
+def run_gpu(inp, k, want_h=False, want_y=False, residual=None, **extra):
+    """One forward through moe_ffn_forward_ex with every debug output (extra:
+    further options of the binding, passed through)."""
     x, wr, w1, w3, w2 = inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"]
     T, d = x.shape
     E, _, f = w1.shape
@@ -45,7 +46,8 @@ def run_gpu(inp, k, want_h=False, want_y=False, residual=None):
     out = binding.moe_ffn_forward_ex(
         x, wr, w1, w3, w2, k, router_bias=inp.get("bias"), topk_ids=res["ids"],
         topk_weights=res["gates"], expert_counts=res["counts"], expert_offsets=res["offsets"],
-        row_token=res["row_token"], slot_row=res["slot_row"], h_out=h, y_out=y, residual=residual)
+        row_token=res["row_token"], slot_row=res["slot_row"], h_out=h, y_out=y, residual=residual,
+        **extra)
     torch.cuda.synchronize()
     res["out"] = out
     res["h"] = h

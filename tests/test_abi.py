@@ -107,6 +107,35 @@ def test_ex_rejects_small_workspace(binding):
     assert "workspace" in binding.moe_ffn_last_error()
 
 
+@pytest.mark.parametrize("eps,xn,status", [
+    (-1.0, 0, 1),                  # negative eps
+    (float("nan"), 0, 1),
+    (float("inf"), 0, 1),
+    (1e-5, ALIGNED, 1),            # x_norm_out == x
+    (1e-5, MISALIGNED, 2),
+])
+def test_ex_rmsnorm_input_validation(binding, eps, xn, status):
+    opts = binding.MoeFfnOpts()
+    opts.dtype = binding.MOE_DTYPE_BF16
+    opts.rmsnorm_input = 1
+    opts.rmsnorm_eps = eps
+    opts.x_norm_out = xn or None
+    p = ctypes.c_void_p(ALIGNED)
+    rc = binding.lib.moe_ffn_forward_ex(p, p, p, p, p, 4, 128, 128, 8, 2, p, None, ctypes.byref(opts))
+    assert rc == status
+    assert binding.moe_ffn_last_error() != ""
+
+
+def test_read_probe_validation(binding):
+    p = ctypes.c_void_p(ALIGNED)
+    lib = binding.lib
+    assert lib.moe_hbm_read_probe(None, 0, 64, None, None) == binding.MOE_OK
+    assert lib.moe_hbm_read_probe(None, 4096, 64, p, None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_hbm_read_probe(ctypes.c_void_p(MISALIGNED), 4096, 64, p, None) == binding.MOE_ERR_UNSUPPORTED
+    assert lib.moe_hbm_read_probe(p, 4100, 64, p, None) == binding.MOE_ERR_UNSUPPORTED
+    assert lib.moe_hbm_read_probe(p, 4096, 0, p, None) == binding.MOE_ERR_INVALID_ARG
+
+
 def test_rmsnorm_validation(binding):
     p = ctypes.c_void_p(ALIGNED)
     assert binding.lib.moe_rmsnorm(None, None, 0, 64, 1e-5, 0, None) == binding.MOE_OK

@@ -1,5 +1,6 @@
 """A stack of RMSNorm + MoE blocks captured in one HIP graph (through
-torch.cuda.CUDAGraph) replays to the same bits as the eager calls."""
+torch.cuda.CUDAGraph) replays to the same bits as the eager calls, with
+RMSNorm as its own call or formed by the router inside the layer call."""
 import pytest
 import torch
 
@@ -21,18 +22,23 @@ def make_stack(layers, T, d, f, E, k):
     }
 
 
-def run_stack(st, h, x, k):
+def run_stack(st, h, x, k, fused=False):
     h.copy_(st["h0"])
     for w in st["w"]:
-        binding.moe_rmsnorm(h, x, eps=1e-5)
-        binding.moe_ffn_forward_ex(x, w["w_router"], w["w1"], w["w3"], w["w2"], k, out=h,
-                                   residual=h, workspace=st["ws"])
+        if fused:
+            binding.moe_ffn_forward_ex(h, w["w_router"], w["w1"], w["w3"], w["w2"], k, out=h,
+                                       residual=h, rmsnorm_eps=1e-5, workspace=st["ws"])
+        else:
+            binding.moe_rmsnorm(h, x, eps=1e-5)
+            binding.moe_ffn_forward_ex(x, w["w_router"], w["w1"], w["w3"], w["w2"], k, out=h,
+                                       residual=h, workspace=st["ws"])
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("T,d,f", [(300, 256, 512),    # 256-row tile path
                                    (24, 256, 1024)])   # streamed-weight path
-def test_graph_replay_matches_eager(T, d, f):
-    print("\n[case] graph of 4 blocks T=%d d=%d f=%d" % (T, d, f), flush=True)
+def test_graph_replay_matches_eager(T, d, f, fused):
+    print("\n[case] graph of 4 blocks T=%d d=%d f=%d fused=%s" % (T, d, f, fused), flush=True)
     E, k = 8, 2
     st = make_stack(4, T, d, f, E, k)
     h = torch.empty_like(st["h0"])
@@ -40,16 +46,21 @@ def test_graph_replay_matches_eager(T, d, f):
     run_stack(st, h, x, k)
     torch.cuda.synchronize()
     ref = h.clone()
+    if fused:
+        # the fused block gives the same bits as RMSNorm then the layer
+        run_stack(st, h, x, k, fused=True)
+        torch.cuda.synchronize()
+        assert torch.equal(h.view(torch.int16), ref.view(torch.int16))
 
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        run_stack(st, h, x, k)
+        run_stack(st, h, x, k, fused)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        run_stack(st, h, x, k)
+        run_stack(st, h, x, k, fused)
     torch.cuda.synchronize()
 
     for rep in range(4):
@@ -58,6 +69,6 @@ def test_graph_replay_matches_eager(T, d, f):
         torch.cuda.synchronize()
         assert torch.equal(h.view(torch.int16), ref.view(torch.int16)), "replay %d differs" % rep
         # eager work between replays, on the same buffers
-        run_stack(st, h, x, k)
+        run_stack(st, h, x, k, fused)
         torch.cuda.synchronize()
         assert torch.equal(h.view(torch.int16), ref.view(torch.int16))

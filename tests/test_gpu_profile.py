@@ -1,5 +1,7 @@
-"""Per-stage timing through moe_ffn_profile_begin/end: call count, stage mask,
-and stages a call skips reporting no time."""
+"""Measurement aids: per-stage timing through moe_ffn_profile_begin/end (call
+count, stage mask, stages a call skips reporting no time) and the streaming
+read probe."""
+import numpy as np
 import pytest
 import torch
 
@@ -50,3 +52,20 @@ def test_profile_stages(T, f, skipped):
     torch.cuda.synchronize()
     _, calls = binding.moe_ffn_profile_end()
     assert calls == 1
+
+
+@pytest.mark.parametrize("n_words,blocks", [(4, 1), (1 << 18, 64), ((1 << 20) + 12, 1000)])
+def test_read_probe_reads_every_word(n_words, blocks):
+    """The streaming-read probe folds every 32-bit word of the buffer exactly
+    once (XOR of all words), for grids smaller and larger than the data."""
+    from sparse_mixture_experts_select_amd import binding
+    print("\n[case] read probe %d words, %d workgroups" % (n_words, blocks), flush=True)
+    g = torch.Generator().manual_seed(n_words)
+    host = torch.randint(-2 ** 31, 2 ** 31 - 1, (n_words,), dtype=torch.int64, generator=g)
+    host = host.to(torch.int32)
+    buf = host.cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    binding.moe_hbm_read_probe(buf, blocks, sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert sink.cpu().numpy().view(np.uint32)[0] == want
