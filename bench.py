@@ -385,10 +385,20 @@ def cpu_baseline(res, seconds, inputs):
                     break
     except OSError:
         pass
+    # Every token runs k experts of the same shape, so the oracle's cost per
+    # token is the same in every workload; full-size figures are that times
+    # the token count (extrapolated, not timed).
+    per_tok = el / (reps * n_tok)
+    full = {}
+    for name in ("decode", "prefill", "skewed", "stack"):
+        w = inputs.WORKLOADS[name]
+        full[name] = round(per_tok * w.T * getattr(w, "layers", 1), 1)
     return {"value": round(tok_s, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle", "cpu_model": cpu_model, "ram_gb": ram_gb, "nproc": os.cpu_count(),
             "sample": "%s workload, tokens 0..%d (full layer per token in fp64), %d passes, %.1f s"
-                      % (wl.name, n_tok - 1, reps, el)}
+                      % (wl.name, n_tok - 1, reps, el),
+            "seconds_per_token_layer": round(per_tok, 5),
+            "extrapolated_full_workload_seconds": full}
 
 
 def read_probe(torch, binding, nbytes=4 << 30, reps=3):
