@@ -68,18 +68,20 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
             // 2 or 4 row fragments of 16.
             p.variant = GEMM_STREAM;
             p.mf = R <= 12 * E ? 1 : (R <= 24 * E ? 2 : 4);
-            const int64_t nt2 = (d + 127) / 128;
             int64_t mt = (R + 16 * p.mf - 1) / (16 * p.mf);
             if (mt < busy_experts) mt = busy_experts;
-            const int64_t tiles = nt2 * mt;
             // GEMM 1 gives each wave a 128-column slab over all of K; when
             // that leaves most CUs idle (one or two tokens), split K over the
             // waves of a workgroup instead.
             p.g1_ksplit = p.mf == 1 && mt * ((f + 511) / 512) < 128;
-            // GEMM 2 runs one slab per workgroup with the K range split over
-            // its 4 waves; cut K further across workgroups only when that
-            // leaves fewer than ~1000 waves streaming.
-            int64_t s = (256 + tiles - 1) / tiles;
+            // GEMM 2 gives each wave a 128-column slab, the 4 waves of a
+            // workgroup 4 adjacent slabs (512 contiguous columns of every w2
+            // row, as GEMM 1 reads w1 and w3), and cuts K across workgroups
+            // so about 256 workgroups stream; the combine adds the K-slice
+            // partials (measured at decode: 162 vs 170 us for one slab per
+            // workgroup with K split over its waves).
+            const int64_t tiles2 = ((d + 511) / 512) * mt;
+            int64_t s = (256 + tiles2 - 1) / tiles2;
             int64_t smax = f / 128;
             if (smax > 16) smax = 16;
             if (smax < 1) smax = 1;

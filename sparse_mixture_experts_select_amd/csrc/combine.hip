@@ -64,11 +64,12 @@ template <> struct Io16<float> {
 };
 
 // One token per workgroup iteration; each thread takes 4 float4 columns
-// (256 apart) of every pick at once, so all of a token's loads are in flight
-// together.  Per column the sum order is fixed: for each pick j = 0..k-1 in
-// slot order, its K slices s = 0..splits-1 summed first, then g_j times that
-// added to the running sum.
-template <typename T>
+// (256 apart).  With one K slice (MULTI false) the loads of every pick are in
+// flight together; with several, a pick's slices are loaded four at a time.
+// Per column the sum order is fixed: for each pick j = 0..k-1 in slot order,
+// its K slices s = 0..splits-1 summed first, then g_j times that added to the
+// running sum.
+template <typename T, bool MULTI>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int splits,
                                                       size_t split_stride,
                                                       const float* __restrict__ gates,
@@ -89,31 +90,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             float4 acc[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (MULTI) {
+                for (int j = 0; j < k; ++j) {
+                    // (row and gate re-read per pick: a runtime index into
+                    // rows[] / g[] would not stay in registers)
+                    const float* yr = y + (size_t)slot_row[(size_t)t * k + j] * d;
+                    const float gj = gates[(size_t)t * k + j];
+                    float4 sv[U];
+                    for (int p0 = 0; p0 < splits; p0 += 4) {
+                        float4 v[4][U];
 #pragma unroll
-            for (int j = 0; j < kMaxPicks; ++j) {
-                if (j >= k) break;
-                const float4* yr = reinterpret_cast<const float4*>(y + (size_t)rows[j] * d);
-                float4 sv[U];
+                        for (int q = 0; q < 4; ++q) {
+                            const float4* yq = reinterpret_cast<const float4*>(yr + (size_t)(p0 + q) * split_stride);
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + 256 * u;
-                    sv[u] = c < d4 ? yr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+                            for (int u = 0; u < U; ++u) {
+                                const int c = c0 + 256 * u;
+                                v[q][u] = (p0 + q < splits && c < d4) ? yq[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+                            }
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            if (p0 + q >= splits) break;
+#pragma unroll
+                            for (int u = 0; u < U; ++u) {
+                                if (p0 + q == 0) {
+                                    sv[u] = v[q][u];
+                                } else {
+                                    sv[u].x += v[q][u].x; sv[u].y += v[q][u].y;
+                                    sv[u].z += v[q][u].z; sv[u].w += v[q][u].w;
+                                }
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        acc[u].x += gj * sv[u].x; acc[u].y += gj * sv[u].y;
+                        acc[u].z += gj * sv[u].z; acc[u].w += gj * sv[u].w;
+                    }
                 }
-                for (int p = 1; p < splits; ++p) {
-                    const float4* yp = reinterpret_cast<const float4*>(y + p * split_stride + (size_t)rows[j] * d);
+            } else {
+#pragma unroll
+                for (int j = 0; j < kMaxPicks; ++j) {
+                    if (j >= k) break;
+                    const float4* yr = reinterpret_cast<const float4*>(y + (size_t)rows[j] * d);
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int c = c0 + 256 * u;
-                        if (c < d4) {
-                            const float4 v = yp[c];
-                            sv[u].x += v.x; sv[u].y += v.y; sv[u].z += v.z; sv[u].w += v.w;
-                        }
+                        const float4 sv = c < d4 ? yr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+                        acc[u].x += g[j] * sv.x; acc[u].y += g[j] * sv.y;
+                        acc[u].z += g[j] * sv.z; acc[u].w += g[j] * sv.w;
                     }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    acc[u].x += g[j] * sv[u].x; acc[u].y += g[j] * sv[u].y;
-                    acc[u].z += g[j] * sv[u].z; acc[u].w += g[j] * sv[u].w;
                 }
             }
 #pragma unroll
@@ -170,12 +196,21 @@ hipError_t launch_combine(int dtype, const float* y, int splits, const float* ga
     int blocks = T < 16384 ? T : 16384;
     if (blocks < 1) blocks = 1;
     const size_t split_stride = (size_t)R * d;
-    if (dtype == 0)
-        hipLaunchKernelGGL(combine_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, y, splits,
-                           split_stride, gates, slot_row, residual, T, d, k, out);
-    else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, y, splits,
-                           split_stride, gates, slot_row, residual, T, d, k, out);
+    if (dtype == 0) {
+        if (splits > 1)
+            hipLaunchKernelGGL((combine_kernel<bf16, true>), dim3(blocks), dim3(256), 0, stream, y,
+                               splits, split_stride, gates, slot_row, residual, T, d, k, out);
+        else
+            hipLaunchKernelGGL((combine_kernel<bf16, false>), dim3(blocks), dim3(256), 0, stream, y,
+                               splits, split_stride, gates, slot_row, residual, T, d, k, out);
+    } else {
+        if (splits > 1)
+            hipLaunchKernelGGL((combine_kernel<float, true>), dim3(blocks), dim3(256), 0, stream, y,
+                               splits, split_stride, gates, slot_row, residual, T, d, k, out);
+        else
+            hipLaunchKernelGGL((combine_kernel<float, false>), dim3(blocks), dim3(256), 0, stream, y,
+                               splits, split_stride, gates, slot_row, residual, T, d, k, out);
+    }
     return hipGetLastError();
 }
 

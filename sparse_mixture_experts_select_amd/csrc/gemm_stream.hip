@@ -11,10 +11,11 @@
 // wavefronts:
 //   KSPLIT_WAVES: one slab; the 4 waves split the slice's K range into 4
 //                 contiguous quarters and add their partial sums in LDS once
-//                 at the end (used when there are few slabs: GEMM 2, and
-//                 GEMM 1 when only a few experts hold rows);
-//   otherwise:    4 adjacent slabs, one per wave, each over the whole K range
-//                 (no reduction; fewer, longer-lived waves, GEMM 1).
+//                 at the end (GEMM 1 when only a few experts hold rows);
+//   otherwise:    4 adjacent slabs, one per wave, each over the slice's whole
+//                 K range (no reduction): every w row is read as 512
+//                 contiguous columns per workgroup (GEMM 1, and GEMM 2 with
+//                 its K range cut into slices across workgroups).
 // GEMM 1 reads its A rows straight from the token rows of x through the
 // row -> token map (no gathered copy of x is made on this path).
 // Each wavefront streams its weight rows straight from HBM into registers:
@@ -248,10 +249,10 @@ hipError_t launch_gemm1_swiglu_stream(const void* x, const int32_t* row_token, c
 hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* offsets, int R, int E,
                                int f, int d, int mf, int splits, float* y, hipStream_t stream) {
     if (mf >= 4)
-        return launch_stream<false, true, 4>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+        return launch_stream<false, false, 4>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
     if (mf == 2)
-        return launch_stream<false, true, 2>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
-    return launch_stream<false, true, 1>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+        return launch_stream<false, false, 2>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
+    return launch_stream<false, false, 1>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits, stream);
 }
 
 }  // namespace moe
