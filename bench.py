@@ -599,10 +599,22 @@ def summarize_trace(trace_dir):
     with open(os.path.join(trace_dir, "run_kernel_trace.csv")) as fh:
         rows = list(csv.DictReader(fh))
     groups = {}
+    phase = None  # the router launch that opened the current layer call
+    garbled = False
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
     for r in rows:
         if "moe" not in r["Kernel_Name"] and "copyBuffer" not in r["Kernel_Name"]:
             continue
-        key = (_short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size_X"]))
+        name = _short_kernel_name(r["Kernel_Name"])
+        if "_Accum" in name:
+            # rocprofv3 prints combine_kernel<bf16, true> (the K-slice form,
+            # the only combine instantiation with a bool true that the
+            # benchmark runs) with this garbled template list
+            name, garbled = "combine_kernel<bf16, true>", True
+        grid = int(r["Grid_Size_X"])
+        if name.startswith("router_topk_kernel"):
+            phase = (name, grid)
+        key = (phase, name, grid)
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         g = groups.setdefault(key, {"d": [], "first": int(r["Dispatch_Id"]), "row": r})
         g["d"].append(dur)
@@ -614,10 +626,14 @@ def summarize_trace(trace_dir):
         fh.write("# command: %s\n" % TRACE_COMMAND)
         fh.write("# summarized by: python3 bench.py --summarize-trace gpurun_out/trace\n")
         fh.write("# calls = warm-up + one routing probe call + timed steps; durations in us; "
-                 "grid in work-items; torch's input generation kernels left out\n")
+                 "grid in work-items; torch's input generation kernels left out; rows are grouped "
+                 "per workload (the router launch that opens each layer call)\n")
+        if garbled:
+            fh.write("# combine_kernel<bf16, true>: rocprofv3 printed this instantiation's name as "
+                     "'combine_kernel<bool _Accum, bool, E>'\n")
         fh.write("%-44s %9s %6s %10s %10s %10s %5s %5s %6s\n" % (
             "kernel", "grid", "calls", "avg_us", "min_us", "max_us", "vgpr", "agpr", "lds"))
-        for (name, grid), g in sorted(groups.items(), key=lambda kv: kv[1]["first"]):
+        for (_, name, grid), g in sorted(groups.items(), key=lambda kv: kv[1]["first"]):
             r = g["row"]
             fh.write("%-44s %9d %6d %10.2f %10.2f %10.2f %5s %5s %6s\n" % (
                 name[:44], grid, len(g["d"]), statistics.mean(g["d"]), min(g["d"]), max(g["d"]),
