@@ -254,7 +254,6 @@ __global__ __launch_bounds__(kBlockThreads) void route_place_kernel(
     }
 }
 
-template <int VEC_BYTES>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
                                                           const int32_t* __restrict__ row_token,
                                                           int R, int vec_per_row,
@@ -273,18 +272,19 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
 // element (r, i) of x_perm [R, d] at ((i / 32) * R + r) * 32 + i % 32, so one
 // 32-wide K block of consecutive rows is one contiguous run.  Thread unit u =
 // (block, row, 16-byte piece) with the piece fastest: writes are contiguous.
+// The tile path keeps x_perm under 2 GiB, so unit numbers fit in 32 bits.
 __global__ __launch_bounds__(256) void gather_rows_kb_kernel(const uint4* __restrict__ x,
                                                              const int32_t* __restrict__ row_token,
                                                              int R, int vec_per_row,
                                                              uint4* __restrict__ x_perm) {
-    const size_t units = (size_t)R * vec_per_row;
-    for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (size_t)gridDim.x * 256) {
-        const int piece = (int)(u & 3);
-        const size_t rb = u >> 2;
-        const int r = (int)(rb % (size_t)R);
-        const int b = (int)(rb / (size_t)R);
+    const uint32_t units = (uint32_t)R * (uint32_t)vec_per_row;
+    const uint32_t ur = (uint32_t)R;
+    for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
+        const uint32_t rb = u >> 2;
+        const uint32_t b = rb / ur;
+        const uint32_t r = rb - b * ur;
         const int t = row_token[r];
-        x_perm[u] = x[(size_t)t * vec_per_row + 4 * b + piece];
+        x_perm[u] = x[(size_t)t * vec_per_row + 4 * b + (u & 3)];
     }
 }
 
@@ -331,8 +331,10 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token
     const int esize = dtype == 0 ? 2 : 4;
     const int vec_per_row = d * esize / 16;
     if (kb) {
-        // bf16 only: 32-element blocks are 4 16-byte pieces (d is a multiple of 64)
+        // bf16 only: 32-element blocks are 4 16-byte pieces (d is a multiple
+        // of 64); the caller keeps R * d * 2 bytes under 2 GiB
         const size_t units = (size_t)R * vec_per_row;
+        if (units >= ((size_t)1 << 31)) return hipErrorInvalidValue;
         size_t blocks = (units + 255) / 256;
         if (blocks > 16384) blocks = 16384;
         if (blocks < 1) blocks = 1;
@@ -344,7 +346,7 @@ hipError_t launch_gather_rows(int dtype, const void* x, const int32_t* row_token
     int blocks = (R + 3) / 4;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(gather_rows_kernel<16>, dim3(blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(256), 0, stream,
                        reinterpret_cast<const uint4*>(x), row_token, R, vec_per_row,
                        reinterpret_cast<uint4*>(x_perm));
     return hipGetLastError();
