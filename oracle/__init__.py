@@ -46,7 +46,7 @@ def build(force: bool = True) -> str:
     os.makedirs(_BUILD_DIR, exist_ok=True)
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+           "-Wall", "-Wextra", "-I", _HERE, _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH

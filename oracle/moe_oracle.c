@@ -40,12 +40,11 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include "moe_oracle.h"
 #ifdef _OPENMP
 #include <omp.h>
 #endif
-
-#define ORACLE_F32 0
-#define ORACLE_BF16 1
 
 /* Widen element i of a binary32 or bfloat16 array to double (exact). */
 static double elem(const void *base, int dtype, int64_t i)

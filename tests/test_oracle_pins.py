@@ -57,8 +57,9 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     cfile = tmp_path / "mutant.c"
     cfile.write_text(mutated)
     so = tmp_path / "libmutant.so"
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", str(cfile),
-                    "-o", str(so), "-lm"], check=True)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                    "-I", os.path.dirname(oracle.__file__), str(cfile), "-o", str(so), "-lm"],
+                   check=True)
     mutant = oracle.configure(ctypes.CDLL(str(so)))
     saved = oracle._load()
     oracle._lib = mutant
