@@ -64,6 +64,9 @@ SMALL = [
     (1500, 1024, 2048, 8, 2, torch.bfloat16), # GEMM 2 tiles cut into 3 K pieces, several per XCD
     (50, 100, 60, 5, 2, torch.float32),
     (200, 64, 96, 16, 4, torch.float32),
+    # multi-workgroup route scan (over 4096 assignments) with wide routing
+    (700, 128, 128, 64, 8, torch.bfloat16),
+    (1100, 64, 96, 8, 4, torch.float32),      # and fp32 router with 4 tokens per workgroup
 ]
 
 
