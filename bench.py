@@ -47,16 +47,18 @@ GEMM1_KERNEL = {
     "skewed": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
 }
 CALIBRATION_BYTES = 1 << 30
-PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d gpurun_out/pmc_{tag} -o run -- "
+# Profiling commands behind the committed summaries; {out} is the rocprofv3
+# output directory that the summarizer is then pointed at.
+PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d {out} -o run -- "
                "python3 bench.py --steps 3 --warmup 1 --stack off --skewed off --no-cpu-baseline "
                "--calibrate-copy")
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE GRBM_COUNT"
 MFMA_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv "
-                "-d gpurun_out/pmc_mfma -o run -- python3 bench.py --workload prefill --secondary none "
+                "-d {out} -o run -- python3 bench.py --workload prefill --secondary none "
                 "--steps 3 --warmup 1 --stack off --skewed off --no-cpu-baseline")
 SIMDS = 256 * 4          # MI355X: 256 CUs x 4 SIMDs
 NOMINAL_CLOCK_HZ = 2.4e9  # the clock the 2.5 PFLOP/s figure assumes
-TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o run -- "
+TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d {out} -o run -- "
                  "python3 bench.py --steps 10 --warmup 2 --cpu-seconds 2")
 
 
@@ -479,11 +481,10 @@ def summarize_counters(fetch_dir, write_dir):
         with open(out, "w") as fh:
             fh.write("# HBM traffic of the w1/w3 grouped GEMM + SwiGLU kernel, %s workload\n" % wl)
             fh.write("# kernel: %s (source %s)\n" % (pattern, src))
-            for name in ("FETCH_SIZE", "WRITE_SIZE"):
-                fh.write("# command (%s): %s\n" % (name, PMC_COMMAND.format(
-                    counter=name, tag=name.split("_")[0].lower())))
-            fh.write("# summarized by: python3 bench.py --summarize-counters gpurun_out/pmc_fetch "
-                     "gpurun_out/pmc_write\n")
+            for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+                fh.write("# command (%s): %s\n" % (name, PMC_COMMAND.format(counter=name, out=d)))
+            fh.write("# summarized by: python3 bench.py --summarize-counters %s %s\n"
+                     % (fetch_dir, write_dir))
             fh.write("# calibration: %d-byte device copy reads FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f "
                      "KiB\n" % (CALIBRATION_BYTES, calib["FETCH_SIZE"], calib["WRITE_SIZE"]))
             fh.write("fetch_scale = %.4f\n" % factor["FETCH_SIZE"])
@@ -533,8 +534,8 @@ def summarize_mfma(run_dir):
         fh.write("# MFMA use of the w1/w3 grouped GEMM + SwiGLU kernel, prefill workload "
                  "(T=4096, d=4096, f=14336, E=8, k=2, bf16)\n")
         fh.write("# kernel: %s (source %s)\n" % (pattern, GEMM1_KERNEL["prefill"][0]))
-        fh.write("# command: %s\n" % MFMA_COMMAND)
-        fh.write("# summarized by: python3 bench.py --summarize-mfma gpurun_out/pmc_mfma\n")
+        fh.write("# command: %s\n" % MFMA_COMMAND.format(out=run_dir))
+        fh.write("# summarized by: python3 bench.py --summarize-mfma %s\n" % run_dir)
         fh.write("# counters per launch (averages over %d launches); SQ_VALU_MFMA_BUSY_CYCLES is "
                  "summed over all %d SIMDs (a 16x16x32 bf16 MFMA keeps its SIMD busy 16 cycles)\n"
                  % (len(span), SIMDS))
@@ -623,8 +624,8 @@ def summarize_trace(trace_dir):
         fh.write("# rocprofv3 kernel trace of the benchmark: decode (T=32), prefill (T=4096), "
                  "skewed routing (T=16384), then the 32-block stack (T=2048; one layer call per "
                  "block, RMSNorm formed by the router); d=4096 f=14336 E=8 k=2 bf16\n")
-        fh.write("# command: %s\n" % TRACE_COMMAND)
-        fh.write("# summarized by: python3 bench.py --summarize-trace gpurun_out/trace\n")
+        fh.write("# command: %s\n" % TRACE_COMMAND.format(out=trace_dir))
+        fh.write("# summarized by: python3 bench.py --summarize-trace %s\n" % trace_dir)
         fh.write("# calls = warm-up + one routing probe call + timed steps; durations in us; "
                  "grid in work-items; torch's input generation kernels left out; rows are grouped "
                  "per workload (the router launch that opens each layer call)\n")
