@@ -85,6 +85,43 @@ def layer_algorithmic(wl, counts):
     return flops, nbytes
 
 
+def stage_rooflines(wl, counts, stage_ms, decode):
+    """Each stage of the layer against its own roofline, from the per-stage
+    times of the breakdown pass (HIP events at the stage boundaries, so a
+    stage's time includes its launch gap) and the stage's algorithmic bytes
+    or flops: the router reads x and W_r and writes ids and gates; the scan
+    is a latency-bound pass over T*k ids; the gather reads and writes every
+    grouped row once; GEMM 1 and GEMM 2 are weight-stream bound at decode and
+    MFMA bound otherwise; the combine reads one fp32 expert output per row and
+    writes out."""
+    R = wl.T * wl.k
+    active = int((counts > 0).sum())
+    hbm = {
+        "router_topk": wl.T * wl.d * 2 + wl.d * wl.E * 2 + R * 8,
+        "gather_rows": 2 * R * wl.d * 2,
+        "combine": R * wl.d * 4 + wl.T * wl.d * 2 + R * 8,
+    }
+    if decode:
+        hbm["gemm1_swiglu"] = active * 2 * wl.d * wl.f * 2 + R * wl.d * 2 + R * wl.f * 2
+        hbm["gemm2"] = active * wl.f * wl.d * 2 + R * wl.f * 2 + R * wl.d * 4
+    flops = {} if decode else {"gemm1_swiglu": 4.0 * R * wl.d * wl.f, "gemm2": 2.0 * R * wl.f * wl.d}
+    out = {}
+    for stage, ms in stage_ms.items():
+        if stage in hbm:
+            a = hbm[stage] / (ms * 1e-3) / 1e9
+            # bytes that 8 TB/s moves in under 2 us: launch latency bounds it
+            bound = "hbm" if hbm[stage] / (HBM_PEAK_GBS * 1e9) >= 2e-6 else "latency"
+            out[stage] = {"bound": bound, "ms": ms, "achieved": round(a, 1), "unit": "GB/s",
+                          "frac": round(a / HBM_PEAK_GBS, 4)}
+        elif stage in flops:
+            a = flops[stage] / (ms * 1e-3) / 1e12
+            out[stage] = {"bound": "mfma", "ms": ms, "achieved": round(a, 1), "unit": "TFLOP/s",
+                          "frac": round(a / MFMA_BF16_PEAK_TFLOPS, 4)}
+        else:
+            out[stage] = {"bound": "latency", "ms": ms}
+    return out
+
+
 def source_digest(workload):
     """Digest of the source of the w1/w3 kernel the workload runs (plus the
     shared header), to tell whether committed counter figures still apply."""
@@ -179,6 +216,8 @@ def run_workload(name, steps, warmup, binding, inputs, torch):
         "ms_per_step": ms_per_step,
         "tokens_per_s": wl.T / (ms_per_step * 1e-3),
         "stage_ms": {kk: round(v, 5) for kk, v in stage_avg.items()},  # breakdown pass
+        "stage_roofline": stage_rooflines(wl, counts_h, {kk: round(v, 5) for kk, v in stage_avg.items()},
+                                          name == "decode"),
         "step_ms": step_dist,  # distribution pass
         "counts": counts_h.tolist(),
         "gemm1_ms": g_ms,
@@ -710,6 +749,7 @@ def main():
                   "hbm_gbs": round(prim["layer_gbs"], 1),
                   "hbm_frac": round(prim["layer_gbs"] / HBM_PEAK_GBS, 4)},
         "stages_ms": prim["stage_ms"],
+        "stages_roofline": prim["stage_roofline"],
         "step_ms": prim["step_ms"],
         "note": ("each step streams the expert weights from HBM: one layer's 2.82 GB exceeds the "
                  "256 MiB MALL, so no cache flush is needed between steps"),
@@ -730,6 +770,7 @@ def main():
                       "mfma_frac": round(res["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
                       "hbm_gbs": round(res["layer_gbs"], 1)},
             "stages_ms": res["stage_ms"],
+            "stages_roofline": res["stage_roofline"],
             "step_ms": res["step_ms"],
         }
         if name == "skewed":

@@ -23,7 +23,7 @@
 //
 // Fused RMSNorm (NORM): the input rows are the residual stream h of the
 // stacked block h = h + MoE(RMSNorm(h)).  A first pass over the row forms
-// its sum of squares, the second scales each 16-byte slice by
+// its sum of squares (keeping the slices in registers), the second scales each 16-byte slice by
 // 1/sqrt(mean + eps), rounds it once to the storage type, stores it as the
 // layer input x, and takes the logits from those rounded values.  The sum of
 // squares is accumulated in the same order as rmsnorm_kernel (the same
@@ -37,15 +37,19 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxK = 8;
+// Fused RMSNorm: the first kNormCache 16-byte slices of each of a lane's rows
+// stay in registers between the two passes (all of a row up to d = 4096 in
+// bf16), so the second pass reloads only what lies past them.
+constexpr int kNormCache = 2;
 
 template <typename T> struct Vec;
 template <> struct Vec<bf16> {
     static constexpr int N = 8;  // elements per 16-byte load
-    __device__ static void load(const bf16* p, float* v) {
-        uint4 q = *reinterpret_cast<const uint4*>(p);
+    __device__ static void unpack(const uint4& q, float* v) {
         v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
         v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
     }
+    __device__ static void load(const bf16* p, float* v) { unpack(*reinterpret_cast<const uint4*>(p), v); }
     __device__ static float one(const bf16* p, size_t i) { return (float)p[i]; }
     // v <- round(v * r), stored to p; v keeps the rounded values.
     __device__ static void scale_store(float* v, float r, bf16* p) {
@@ -61,10 +65,11 @@ template <> struct Vec<bf16> {
 };
 template <> struct Vec<float> {
     static constexpr int N = 4;
-    __device__ static void load(const float* p, float* v) {
-        float4 q = *reinterpret_cast<const float4*>(p);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    __device__ static void unpack(const uint4& q, float* v) {
+        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
     }
+    __device__ static void load(const float* p, float* v) { unpack(*reinterpret_cast<const uint4*>(p), v); }
     __device__ static float one(const float* p, size_t i) { return p[i]; }
     __device__ static void scale_store(float* v, float r, float* p) {
 #pragma unroll
@@ -123,11 +128,27 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
 
     // RMSNorm scale of each token (NORM only).
     float rs[TPW];
+    uint4 cache[NORM ? kNormCache : 1][TPW];
     if constexpr (NORM) {
         float ss[TPW];
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) ss[tt] = 0.0f;
-        for (int i0 = threadIdx.x * VN; i0 < d; i0 += kThreads * VN) {
+        // slices in ascending order, the cached ones first
+#pragma unroll
+        for (int n = 0; n < kNormCache; ++n) {
+            const int i0 = threadIdx.x * VN + n * kThreads * VN;
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                if (i0 < d && t0 + tt < T_) {
+                    cache[n][tt] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * d + i0);
+                    float v[VN];
+                    Vec<T>::unpack(cache[n][tt], v);
+#pragma unroll
+                    for (int u = 0; u < VN; ++u) ss[tt] = fmaf(v[u], v[u], ss[tt]);
+                }
+            }
+        }
+        for (int i0 = threadIdx.x * VN + kNormCache * kThreads * VN; i0 < d; i0 += kThreads * VN) {
 #pragma unroll
             for (int tt = 0; tt < TPW; ++tt) {
                 if (t0 + tt < T_) {
@@ -154,18 +175,8 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) acc[tt][e] = 0.0f;
 
-    for (int i0 = (wave * 64 + lane) * VN; i0 < d; i0 += kThreads * VN) {
-        float xv[TPW][VN];
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            if (t0 + tt < T_) {
-                Vec<T>::load(x + (size_t)(t0 + tt) * d + i0, xv[tt]);
-                if constexpr (NORM) Vec<T>::scale_store(xv[tt], rs[tt], xn + (size_t)(t0 + tt) * d + i0);
-            } else {
-#pragma unroll
-                for (int u = 0; u < VN; ++u) xv[tt][u] = 0.0f;
-            }
-        }
+    // Partial logits of this lane's slice at i0 for the TPW tokens in xv.
+    auto accumulate = [&](int i0, float (&xv)[TPW][VN]) {
         if (ROWS8) {
 #pragma unroll
             for (int u = 0; u < VN; ++u) {
@@ -189,6 +200,43 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
                 }
             }
         }
+    };
+    int i_rest = (wave * 64 + lane) * VN;  // first slice not taken from the cache
+    if constexpr (NORM) {
+        // (called once per cached slice, so every cache index is a constant)
+        auto from_cache = [&](int i0, const uint4 (&c)[TPW]) {
+            if (i0 >= d) return;
+            float xv[TPW][VN];
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                if (t0 + tt < T_) {
+                    Vec<T>::unpack(c[tt], xv[tt]);
+                    Vec<T>::scale_store(xv[tt], rs[tt], xn + (size_t)(t0 + tt) * d + i0);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < VN; ++u) xv[tt][u] = 0.0f;
+                }
+            }
+            accumulate(i0, xv);
+        };
+        static_assert(kNormCache == 2, "one from_cache call per cached slice");
+        from_cache(i_rest, cache[0]);
+        from_cache(i_rest + kThreads * VN, cache[1]);
+        i_rest += kNormCache * kThreads * VN;
+    }
+    for (int i0 = i_rest; i0 < d; i0 += kThreads * VN) {
+        float xv[TPW][VN];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            if (t0 + tt < T_) {
+                Vec<T>::load(x + (size_t)(t0 + tt) * d + i0, xv[tt]);
+                if constexpr (NORM) Vec<T>::scale_store(xv[tt], rs[tt], xn + (size_t)(t0 + tt) * d + i0);
+            } else {
+#pragma unroll
+                for (int u = 0; u < VN; ++u) xv[tt][u] = 0.0f;
+            }
+        }
+        accumulate(i0, xv);
     }
 
     // Wave sums of the TPW x EMAX partial logits (acc[tt][e] stays 0 for
@@ -286,7 +334,9 @@ hipError_t dispatch_e(const void* x, const void* wr, const float* bias, int T_, 
     const bool big = T_ > 1024;
     if constexpr (sizeof(T) == 2) {
         if (E == 8) {
-            if (T_ > 2048) return launch_t<T, 8, 8, true>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
+            // (the fused RMSNorm keeps its rows in registers: at most 4 tokens)
+            if (T_ > 2048 && xn == nullptr)
+                return launch_t<T, 8, 8, true>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
             if (T_ > 768) return launch_t<T, 8, 4, true>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
             if (T_ > 384) return launch_t<T, 8, 2, true>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
             return launch_t<T, 8, 1, true>(x, wr, bias, T_, d, E, k, ids, gates, xn, eps, stream);
