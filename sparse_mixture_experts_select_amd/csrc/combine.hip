@@ -18,7 +18,8 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxPicks = 8;  // k <= 8 (checked by the entry points)
+constexpr int kMaxPicks = 8;    // k <= 8 (checked by the entry points)
+constexpr int kMaxSlices = 16;  // K-slice partials of y (the host plans at most 16)
 
 template <typename T> struct Io;
 template <> struct Io<bf16> {
@@ -64,14 +65,11 @@ template <> struct Io16<float> {
 };
 
 // One token per workgroup iteration; each thread takes 4 float4 columns
-// (256 apart).  With one K slice (MULTI false) the loads of every pick are in
-// flight together; with several, a pick's slices are loaded four at a time.
-// Per column the sum order is fixed: for each pick j = 0..k-1 in slot order,
-// its K slices s = 0..splits-1 summed first, then g_j times that added to the
-// running sum.
-template <typename T, bool MULTI>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int splits,
-                                                      size_t split_stride,
+// (256 apart) of every pick at once, so all of a token's loads are in flight
+// together.  Per column the sum order is fixed: picks j = 0..k-1 in slot
+// order, g_j times the expert output added to the running sum (from zero).
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ slot_row,
                                                       const void* residual, int Tn, int d, int k,
@@ -90,56 +88,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             float4 acc[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if constexpr (MULTI) {
-                for (int j = 0; j < k; ++j) {
-                    // (row and gate re-read per pick: a runtime index into
-                    // rows[] / g[] would not stay in registers)
-                    const float* yr = y + (size_t)slot_row[(size_t)t * k + j] * d;
-                    const float gj = gates[(size_t)t * k + j];
-                    float4 sv[U];
-                    for (int p0 = 0; p0 < splits; p0 += 4) {
-                        float4 v[4][U];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float4* yq = reinterpret_cast<const float4*>(yr + (size_t)(p0 + q) * split_stride);
+            for (int j = 0; j < kMaxPicks; ++j) {
+                if (j >= k) break;
+                const float4* yr = reinterpret_cast<const float4*>(y + (size_t)rows[j] * d);
 #pragma unroll
-                            for (int u = 0; u < U; ++u) {
-                                const int c = c0 + 256 * u;
-                                v[q][u] = (p0 + q < splits && c < d4) ? yq[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-                            }
-                        }
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            if (p0 + q >= splits) break;
-#pragma unroll
-                            for (int u = 0; u < U; ++u) {
-                                if (p0 + q == 0) {
-                                    sv[u] = v[q][u];
-                                } else {
-                                    sv[u].x += v[q][u].x; sv[u].y += v[q][u].y;
-                                    sv[u].z += v[q][u].z; sv[u].w += v[q][u].w;
-                                }
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        acc[u].x += gj * sv[u].x; acc[u].y += gj * sv[u].y;
-                        acc[u].z += gj * sv[u].z; acc[u].w += gj * sv[u].w;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < kMaxPicks; ++j) {
-                    if (j >= k) break;
-                    const float4* yr = reinterpret_cast<const float4*>(y + (size_t)rows[j] * d);
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int c = c0 + 256 * u;
-                        const float4 sv = c < d4 ? yr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-                        acc[u].x += g[j] * sv.x; acc[u].y += g[j] * sv.y;
-                        acc[u].z += g[j] * sv.z; acc[u].w += g[j] * sv.w;
-                    }
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + 256 * u;
+                    const float4 sv = c < d4 ? yr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    acc[u].x += g[j] * sv.x; acc[u].y += g[j] * sv.y;
+                    acc[u].z += g[j] * sv.z; acc[u].w += g[j] * sv.w;
                 }
             }
 #pragma unroll
@@ -156,6 +114,51 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 Io<T>::store4(out, idx, a);
             }
         }
+    }
+}
+
+// The same with y in `splits` K-slice partials (the streamed path's GEMM 2
+// cuts K across workgroups).  One thread per (token, float4 column), columns
+// over blockIdx.x and tokens over blockIdx.y, so a batch of a few tokens
+// still spreads over many workgroups; all of a pick's slices are loaded at
+// once, then added in slice order before g_j times their sum is added.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_slices_kernel(const float* __restrict__ y, int splits,
+                                                             size_t split_stride,
+                                                             const float* __restrict__ gates,
+                                                             const int32_t* __restrict__ slot_row,
+                                                             const void* residual, int Tn, int d,
+                                                             int k, void* out) {
+    const int d4 = d / 4;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= d4) return;
+    const size_t stride4 = split_stride / 4;
+    for (int t = blockIdx.y; t < Tn; t += gridDim.y) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < k; ++j) {
+            const float4* yr = reinterpret_cast<const float4*>(y + (size_t)slot_row[(size_t)t * k + j] * d) + c;
+            const float gj = gates[(size_t)t * k + j];
+            float4 v[kMaxSlices];
+#pragma unroll
+            for (int p = 0; p < kMaxSlices; ++p)
+                if (p < splits) v[p] = yr[p * stride4];
+            float4 sv = v[0];
+#pragma unroll
+            for (int p = 1; p < kMaxSlices; ++p) {
+                if (p < splits) {
+                    sv.x += v[p].x; sv.y += v[p].y; sv.z += v[p].z; sv.w += v[p].w;
+                }
+            }
+            acc.x += gj * sv.x; acc.y += gj * sv.y; acc.z += gj * sv.z; acc.w += gj * sv.w;
+        }
+        const size_t idx = (size_t)t * d4 + c;
+        float a[4] = {acc.x, acc.y, acc.z, acc.w};
+        if (residual != nullptr) {
+            float rv[4];
+            Io<T>::load4(residual, idx, rv);
+            for (int q = 0; q < 4; ++q) a[q] = rv[q] + a[q];
+        }
+        Io<T>::store4(out, idx, a);
     }
 }
 
@@ -193,24 +196,26 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* h, void* x, in
 hipError_t launch_combine(int dtype, const float* y, int splits, const float* gates,
                           const int32_t* slot_row, const void* residual, int T, int d, int k, int R,
                           void* out, hipStream_t stream) {
+    if (splits < 1 || splits > kMaxSlices) return hipErrorInvalidValue;
+    if (splits > 1) {
+        const dim3 grid((unsigned)((d / 4 + 255) / 256), (unsigned)(T < 65535 ? (T > 0 ? T : 1) : 65535));
+        const size_t split_stride = (size_t)R * d;
+        if (dtype == 0)
+            hipLaunchKernelGGL(combine_slices_kernel<bf16>, grid, dim3(256), 0, stream, y, splits,
+                               split_stride, gates, slot_row, residual, T, d, k, out);
+        else
+            hipLaunchKernelGGL(combine_slices_kernel<float>, grid, dim3(256), 0, stream, y, splits,
+                               split_stride, gates, slot_row, residual, T, d, k, out);
+        return hipGetLastError();
+    }
     int blocks = T < 16384 ? T : 16384;
     if (blocks < 1) blocks = 1;
-    const size_t split_stride = (size_t)R * d;
-    if (dtype == 0) {
-        if (splits > 1)
-            hipLaunchKernelGGL((combine_kernel<bf16, true>), dim3(blocks), dim3(256), 0, stream, y,
-                               splits, split_stride, gates, slot_row, residual, T, d, k, out);
-        else
-            hipLaunchKernelGGL((combine_kernel<bf16, false>), dim3(blocks), dim3(256), 0, stream, y,
-                               splits, split_stride, gates, slot_row, residual, T, d, k, out);
-    } else {
-        if (splits > 1)
-            hipLaunchKernelGGL((combine_kernel<float, true>), dim3(blocks), dim3(256), 0, stream, y,
-                               splits, split_stride, gates, slot_row, residual, T, d, k, out);
-        else
-            hipLaunchKernelGGL((combine_kernel<float, false>), dim3(blocks), dim3(256), 0, stream, y,
-                               splits, split_stride, gates, slot_row, residual, T, d, k, out);
-    }
+    if (dtype == 0)
+        hipLaunchKernelGGL(combine_kernel<bf16>, dim3(blocks), dim3(256), 0, stream, y, gates,
+                           slot_row, residual, T, d, k, out);
+    else
+        hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, stream, y, gates,
+                           slot_row, residual, T, d, k, out);
     return hipGetLastError();
 }
 
