@@ -11,8 +11,7 @@
 // Rows of one expert are contiguous and in ascending (token, pick) order, so
 // the permutation is stable and deterministic (no atomics).
 //
-// route_scan_kernel is one workgroup of 16 wavefronts (one wavefront for up
-// to 512 assignments, which it takes in one batch).  Each wave owns a
+// route_scan_kernel is one workgroup of 16 wavefronts.  Each wave owns a
 // contiguous run of 64-assignment chunks.  Pass 1 counts, per expert, with
 // one ballot per expert per chunk; the per-wave counts are scanned in LDS;
 // pass 2 walks the same chunks again and gives each assignment its row as
@@ -33,18 +32,16 @@
 namespace moe {
 namespace {
 
+constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kBatch = 8;  // chunks of 64 ids loaded together per wave
-// up to this many assignments one wavefront takes every chunk in one batch
-constexpr int kScanOneWaveMax = 64 * kBatch;
 // above this many assignments the multi-workgroup form runs
 constexpr int kScanSingleMax = 4096;
 
-template <int kScanThreads>
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     const int32_t* __restrict__ ids, int R, int k, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot_row,
     int32_t* __restrict__ row_token) {
-    constexpr int kScanWaves = kScanThreads / 64;
     __shared__ int wave_count[kScanWaves][64];
     __shared__ int wave_base[kScanWaves][64];
     __shared__ int expert_base[65];
@@ -314,14 +311,8 @@ hipError_t launch_route_scan(const int32_t* ids, int T, int k, int E, int32_t* c
                              int32_t* offsets, int32_t* slot_row, int32_t* row_token,
                              int32_t* scratch, hipStream_t stream) {
     const int R = T * k;
-    if (R <= kScanOneWaveMax) {
-        // a small batch: one wavefront (no idle waves at the barriers)
-        hipLaunchKernelGGL(route_scan_kernel<64>, dim3(1), dim3(64), 0, stream, ids, R, k, E,
-                           counts, offsets, slot_row, row_token);
-        return hipGetLastError();
-    }
     if (R <= kScanSingleMax) {
-        hipLaunchKernelGGL(route_scan_kernel<1024>, dim3(1), dim3(1024), 0, stream, ids, R, k, E,
+        hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, ids, R, k, E,
                            counts, offsets, slot_row, row_token);
         return hipGetLastError();
     }
