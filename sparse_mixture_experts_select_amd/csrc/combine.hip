@@ -88,6 +88,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             float4 acc[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            // the residual is loaded up front, so its loads are in flight with
+            // the expert outputs' (each element is read before this thread
+            // writes it, so residual == out is fine)
+            float rv[U][4];
+            if (residual != nullptr) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + 256 * u;
+                    if (c < d4) Io<T>::load4(residual, (size_t)t * d4 + c, rv[u]);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < kMaxPicks; ++j) {
                 if (j >= k) break;
@@ -106,11 +117,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 if (c >= d4) continue;
                 const size_t idx = (size_t)t * d4 + c;
                 float a[4] = {acc[u].x, acc[u].y, acc[u].z, acc[u].w};
-                if (residual != nullptr) {
-                    float rv[4];
-                    Io<T>::load4(residual, idx, rv);
-                    for (int q = 0; q < 4; ++q) a[q] = rv[q] + a[q];
-                }
+                if (residual != nullptr)
+                    for (int q = 0; q < 4; ++q) a[q] = rv[u][q] + a[q];
                 Io<T>::store4(out, idx, a);
             }
         }
