@@ -15,6 +15,8 @@
 //   6. combine        y, gates, slot_row -> out [T,d] (+ residual)
 // Nothing is read back to the host, so the host never waits for the GPU
 // (except when the cached workspace has to grow).
+#include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
@@ -76,12 +78,21 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
             p.g1_ksplit = p.mf == 1 && mt * ((f + 511) / 512) < 128;
             // GEMM 2 gives each wave a 128-column slab, the 4 waves of a
             // workgroup 4 adjacent slabs (512 contiguous columns of every w2
-            // row, as GEMM 1 reads w1 and w3), and cuts K across workgroups
-            // so about 256 workgroups stream; the combine adds the K-slice
-            // partials (measured at decode: 162 vs 170 us for one slab per
-            // workgroup with K split over its waves).
-            const int64_t tiles2 = ((d + 511) / 512) * mt;
-            int64_t s = (256 + tiles2 - 1) / tiles2;
+            // row, as GEMM 1 reads w1 and w3), and cuts K across workgroups;
+            // the combine adds the K-slice partials.  The cut is sized for
+            // about 208 streaming workgroups (256 with 4 row fragments per
+            // tile), counting the experts expected to hold rows when R
+            // assignments spread evenly over E (the routing itself is not
+            // known on the host; workgroups of empty experts exit at once).
+            // Measured at Mixtral shapes for T = 1..128: 170-230 active
+            // workgroups streamed fastest (decode GEMM 2: 154 us with 3
+            // slices, 161 with 4).
+            const double e_act = std::max(std::min((double)k, (double)E),
+                                          E * (1.0 - std::pow(1.0 - 1.0 / E, (double)R)));
+            const double rows_per = (double)R / e_act;
+            const double mt_act = std::max(1.0, std::ceil(rows_per / (16.0 * p.mf)));
+            const double tiles2 = (double)((d + 511) / 512) * e_act * mt_act;
+            int64_t s = std::lround((p.mf >= 4 ? 256.0 : 208.0) / tiles2);
             int64_t smax = f / 128;
             if (smax > 16) smax = 16;
             if (smax < 1) smax = 1;
