@@ -2,7 +2,7 @@
 
 Test infrastructure: gcc, linked against the HIP runtime, libmoe_ffn.so and
 the CPU oracle (both must be built first).  Called by __graft_entry__.build();
-tests/test_gpu_native.py runs the result on a GPU.
+tests/test_gpu_zz_native.py runs the result on a GPU.
 """
 from __future__ import annotations
 

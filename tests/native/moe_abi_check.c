@@ -4,7 +4,7 @@
  *
  * Test infrastructure: built by __graft_entry__.build() (gcc, linked against
  * the HIP runtime, libmoe_ffn.so and the oracle) and run on a GPU by
- * tests/test_gpu_native.py.  Prints one line per check and exits 0 only if
+ * tests/test_gpu_zz_native.py.  Prints one line per check and exits 0 only if
  * every check passed.
  *
  * Inputs come from a seeded splitmix64 stream (Box-Muller normals), the same
