@@ -442,6 +442,17 @@ def cpu_baseline(res, seconds, inputs):
             "extrapolated_full_workload_seconds": full}
 
 
+def device_facts(torch):
+    """What the runtime reports for GPU 0 (compute units, ISA, memory), beside
+    the 256-CU / 2.4 GHz figures the peaks assume; the clock actually held
+    under load is measured separately (MFMA counter summary)."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "memory_gb": round(p.total_memory / 1e9, 1),
+            "l2_bytes": getattr(p, "L2_cache_size", None)}
+
+
 def read_probe(torch, binding, nbytes=4 << 30, reps=3):
     """Measured streaming-read rate of this GPU: the library's read probe
     (16-byte loads in a grid-stride loop) over a buffer far larger than the
@@ -751,6 +762,7 @@ def main():
         "stages_ms": prim["stage_ms"],
         "stages_roofline": prim["stage_roofline"],
         "step_ms": prim["step_ms"],
+        "device": device_facts(torch),
         "note": ("each step streams the expert weights from HBM: one layer's 2.82 GB exceeds the "
                  "256 MiB MALL, so no cache flush is needed between steps"),
     }
