@@ -276,7 +276,10 @@ def test_skewed_workload():
 def test_stack_workload_teacher_forced():
     """32 blocks h <- h + MoE(RMSNorm(h)), T=2048, each with its own weights.
     Every layer is checked on the GPU's own bf16 input of that layer: RMSNorm
-    and the output on sampled tokens, routing on every token."""
+    and the output on sampled tokens, routing on every token.  Beside that,
+    8 tokens are carried through the blocks by the oracle alone (its own h
+    from h0, no GPU value as input), and the GPU's h after every block is
+    compared with that chain on the tokens whose routing has not differed."""
     from sparse_mixture_experts_select_amd import binding
     wl = inputs.WORKLOADS["stack"]
     T, d, f, E, k = wl.T, wl.d, wl.f, wl.E, wl.k
@@ -310,6 +313,16 @@ def test_stack_workload_teacher_forced():
         gpu_ids = PT.to_np(g["ids"])[free_tok]
         diverged |= np.any(np.sort(fr["ids"], axis=1) != np.sort(gpu_ids, axis=1), axis=1)
         h_free = bf16_bits(inputs.bf16_bits_to_f64(h_free) + fr["out"])
+        keep = ~diverged
+        if keep.any():
+            # the oracle-only chain against the GPU after this block: both
+            # sides round h to bf16 after every block from slightly different
+            # sums, so they may drift apart by up to one bf16 unit (2^-8 of
+            # |h|) per block
+            got_f = PT.out_f64(g["out"][free_idx])[keep]
+            want_f = inputs.bf16_bits_to_f64(h_free)[keep]
+            rel_f = np.abs(got_f - want_f).max() / np.abs(want_f).max()
+            assert rel_f <= (layer + 1) * 2.0 ** -8, "layer %d free-running drift %g" % (layer, rel_f)
         tok = np.sort(rng.choice(T, size=6, replace=False))
         # RMSNorm of this layer's input, against the oracle
         h_tok = inputs.host_array(h[torch.as_tensor(tok, device=DEV)])
