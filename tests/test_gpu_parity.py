@@ -107,8 +107,11 @@ def test_all_logits_tied():
     assert np.all(PT.to_np(g["gates"]) == 0.5)
     np.testing.assert_array_equal(PT.to_np(g["counts"]), [70, 70, 0, 0, 0, 0, 0, 0])
     host = PT.host_inputs(inp)
-    ref_g = np.full((70, 2), 0.5)
-    PT.check_outputs(g, host, np.arange(70), ref_g, 2, torch.bfloat16)
+    logits, _, _ = oracle.route(host["x"], host["w_router"], 2)
+    assert np.all(logits == 0.0)
+    # every pair of experts is a correct top-2 here (28 of them)
+    assert len(PT.valid_topk_sets(logits[0], 2)) == 28
+    PT.check_outputs(g, host, np.arange(70), logits, 2, torch.bfloat16)
 
 
 def test_imbalanced_and_empty_experts():
@@ -171,8 +174,8 @@ def test_residual_and_in_place():
     g = PT.run_gpu(inp, 2, residual=resid)
     host = PT.host_inputs(inp)
     logits, o_ids, _ = oracle.route(host["x"], host["w_router"], 2)
-    _, ref_g = PT.check_routing(g, logits, o_ids, 2)
-    PT.check_outputs(g, host, np.arange(150), ref_g, 2, torch.bfloat16,
+    PT.check_routing(g, logits, o_ids, 2)
+    PT.check_outputs(g, host, np.arange(150), logits, 2, torch.bfloat16,
                      residual=PT.out_f64(resid))
     # out == x is allowed
     x2 = inp["x"].clone()
@@ -331,13 +334,13 @@ def test_stack_workload_teacher_forced():
         assert x_err <= 2 ** -8 * np.abs(x_ref).max(), "layer %d rmsnorm error %g" % (layer, x_err)
         # routing on every token
         logits, o_ids, _ = oracle.route(host["x"], host["w_router"], k)
-        exempt, ref_g = PT.check_routing(g, logits, o_ids, k)
+        exempt = PT.check_routing(g, logits, o_ids, k)
         total_ties += int(exempt.sum())
         # h + MoE(x) on the sampled tokens: the MoE part to the bf16 bar, plus
         # one bf16 rounding of the residual sum
-        ids = PT.to_np(g["ids"])
+        ref_ids, ref_gates = PT.reference_selection(logits, PT.to_np(g["ids"]), tok, k)
         ref = oracle.moe_tokens(host["x"], None, host["w1"], host["w3"], host["w2"], k, tokens=tok,
-                                forced_ids=ids[tok], forced_gates=ref_g[tok])
+                                forced_ids=ref_ids, forced_gates=ref_gates)
         moe_ref = ref["out"]
         want = PT.out_f64(h[torch.as_tensor(tok, device=DEV)]) + moe_ref
         got = PT.out_f64(g["out"][torch.as_tensor(tok, device=DEV)])
