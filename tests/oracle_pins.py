@@ -292,6 +292,26 @@ def check_uniform_routing():
     assert np.all(np.abs(shares - 0.125) < 0.02), shares
 
 
+def check_skewed_routing(T=4096, seed=0):
+    """The skewed workload is defined by its imbalance: additive logit biases
+    [2, 1, 0.5, 0, 0, 0, -0.5, -1] on unit-RMS tokens with an N(0, 1/d)
+    router give the heaviest expert roughly 40% of the T*k assignments.  The
+    oracle's routing of such tokens must show that share (0.35..0.45), follow
+    the bias order (experts 3-5 share the same bias, so they are not
+    ordered among themselves), and give shares that sum to 1."""
+    bias = np.array(inputs.SKEW_BIAS, np.float32)
+    x = inputs.make_x(T, 4096, torch.bfloat16, "cpu", "rms", seed, "skew_stats")
+    wr = inputs.make_router(4096, 8, torch.bfloat16, "cpu", seed, "skew_stats")
+    _, ids, _ = oracle.route(inputs.host_array(x), inputs.host_array(wr), 2, bias=bias)
+    shares = np.bincount(ids.ravel(), minlength=8) / (2.0 * T)
+    assert abs(shares.sum() - 1.0) < 1e-12
+    assert 0.35 <= shares[0] <= 0.45, shares
+    mid = shares[3:6]
+    assert shares[0] > shares[1] > shares[2] > mid.max(), shares
+    assert mid.min() > shares[6] > shares[7], shares
+    return shares
+
+
 def check_parameter_counts():
     """The hyperparameter table's shapes give the pages' ~47B total and ~13B
     active parameters (experts, grouped-query attention, router, norms,
@@ -316,5 +336,5 @@ def check_parameter_counts():
 ALL_FAST_PINS = [
     check_gate_invariants, check_k_distinct, check_brute_force, check_identical_experts,
     check_special_k, check_all_ties, check_bias, check_invariances, check_silu,
-    check_forced, check_rmsnorm,
+    check_forced, check_rmsnorm, check_skewed_routing,
 ]
