@@ -85,6 +85,19 @@ def layer_algorithmic(wl, counts):
     return flops, nbytes
 
 
+def design_traffic(wl, gathered):
+    """HBM bytes per layer of the intermediate tensors the design adds to
+    the algorithmic traffic, each written once and read once: the grouped
+    rows x_perm (bf16; only where the rows are gathered, i.e. the tile
+    path), h (bf16) and y (fp32).  The streamed path writes y as a few K-slice
+    partials, which adds (slices - 1) * R * d * 8 bytes, under 1% of its
+    weight bytes, not counted here."""
+    R = wl.T * wl.k
+    parts = {"x_perm": 2 * R * wl.d * 2 if gathered else 0, "h": 2 * R * wl.f * 2,
+             "y": 2 * R * wl.d * 4}
+    return int(sum(parts.values()))
+
+
 def stage_rooflines(wl, counts, stage_ms, decode):
     """Each stage of the layer against its own roofline, from the per-stage
     times of the breakdown pass (HIP events at the stage boundaries, so a
@@ -289,7 +302,9 @@ def run_stack(steps, warmup, binding, inputs, torch):
                      "avg_launch_ms": round(g_ms, 5), "traffic": None},
         "layer": {"tflops_active": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
                   "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                  "hbm_gbs": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1)},
+                  "hbm_gbs": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
+                  # every block runs the tile path (T*k/E = 512 rows per expert)
+                  "design_bytes_per_layer": design_traffic(wl, True)},
     }
     # The same step replayed from one HIP graph (all 32 blocks captured;
     # the layer calls use a caller workspace, as graph capture requires).
@@ -758,7 +773,8 @@ def main():
         "layer": {"tflops_active": round(prim["layer_tflops"], 2),
                   "mfma_frac": round(prim["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
                   "hbm_gbs": round(prim["layer_gbs"], 1),
-                  "hbm_frac": round(prim["layer_gbs"] / HBM_PEAK_GBS, 4)},
+                  "hbm_frac": round(prim["layer_gbs"] / HBM_PEAK_GBS, 4),
+                  "design_bytes_per_layer": design_traffic(wl, "gather_rows" in prim["stage_ms"])},
         "stages_ms": prim["stage_ms"],
         "stages_roofline": prim["stage_roofline"],
         "step_ms": prim["step_ms"],
@@ -780,7 +796,9 @@ def main():
             "roofline": roofline(res, "hbm" if name == "decode" else "mfma"),
             "layer": {"tflops_active": round(res["layer_tflops"], 2),
                       "mfma_frac": round(res["layer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                      "hbm_gbs": round(res["layer_gbs"], 1)},
+                      "hbm_gbs": round(res["layer_gbs"], 1),
+                      "design_bytes_per_layer": design_traffic(inputs.WORKLOADS[name],
+                                                               "gather_rows" in res["stage_ms"])},
             "stages_ms": res["stage_ms"],
             "stages_roofline": res["stage_roofline"],
             "step_ms": res["step_ms"],

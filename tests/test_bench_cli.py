@@ -34,3 +34,14 @@ def test_stage_rooflines_use_algorithmic_work():
     assert st["gemm1_swiglu"]["bound"] == "mfma"
     assert abs(st["gemm1_swiglu"]["achieved"] - 4.0 * R * wl.d * wl.f / 2e-3 / 1e12) < 0.1
     assert st["route_scan"] == {"bound": "latency", "ms": 0.01}
+
+
+def test_design_traffic_counts_intermediates():
+    sys.path.insert(0, ROOT)
+    import bench
+    from sparse_mixture_experts_select_amd import inputs
+    wl = inputs.WORKLOADS["prefill"]
+    R = wl.T * wl.k
+    # x_perm and h in bf16, y in fp32, each written once and read once
+    assert bench.design_traffic(wl, True) == 4 * R * (wl.d + wl.f) + 8 * R * wl.d
+    assert bench.design_traffic(wl, False) == 4 * R * wl.f + 8 * R * wl.d
