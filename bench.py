@@ -52,6 +52,11 @@ CALIBRATION_BYTES = 1 << 30
 PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d {out} -o run -- "
                "python3 bench.py --steps 3 --warmup 1 --stack off --skewed off --no-cpu-baseline "
                "--calibrate-copy")
+# The skewed workload runs the same w1/w3 kernel as prefill, so its counters
+# come from a run of their own.
+SKEWED_PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d {out} "
+                      "-o run -- python3 bench.py --workload skewed --secondary none --steps 3 "
+                      "--warmup 1 --stack off --no-cpu-baseline --calibrate-copy")
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE GRBM_COUNT"
 MFMA_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv "
                 "-d {out} -o run -- python3 bench.py --workload prefill --secondary none "
@@ -511,11 +516,13 @@ def _counter_rows(run_dir):
         return list(csv.DictReader(fh))
 
 
-def summarize_counters(fetch_dir, write_dir):
+def summarize_counters(fetch_dir, write_dir, skewed=False):
     """Turn two rocprofv3 --pmc runs of PMC_COMMAND (FETCH_SIZE, then
-    WRITE_SIZE) into profiles/gemm1_swiglu_<workload>_traffic.txt: HBM bytes
-    per launch of the w1/w3 kernel, each counter scaled by what it reads for
-    the 1 GiB calibration copies run in the same process."""
+    WRITE_SIZE) into profiles/gemm1_swiglu_<workload>_traffic.txt for the
+    decode and prefill workloads, or two runs of SKEWED_PMC_COMMAND into the
+    skewed workload's: HBM bytes per launch of the w1/w3 kernel, each counter
+    scaled by what it reads for the 1 GiB calibration copies run in the same
+    process."""
     import re
     import statistics
 
@@ -537,7 +544,7 @@ def summarize_counters(fetch_dir, write_dir):
                     if r["Counter_Name"] == name and re.search(pattern, r["Kernel_Name"])]
             if vals:
                 per[name] = vals
-        if len(per) != 2 or wl == "skewed":
+        if len(per) != 2 or (wl == "skewed") != skewed:
             continue
         fetch_kib = statistics.mean(per["FETCH_SIZE"])
         write_kib = statistics.mean(per["WRITE_SIZE"])
@@ -546,10 +553,11 @@ def summarize_counters(fetch_dir, write_dir):
         with open(out, "w") as fh:
             fh.write("# HBM traffic of the w1/w3 grouped GEMM + SwiGLU kernel, %s workload\n" % wl)
             fh.write("# kernel: %s (source %s)\n" % (pattern, src))
+            cmd = SKEWED_PMC_COMMAND if skewed else PMC_COMMAND
             for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-                fh.write("# command (%s): %s\n" % (name, PMC_COMMAND.format(counter=name, out=d)))
-            fh.write("# summarized by: python3 bench.py --summarize-counters %s %s\n"
-                     % (fetch_dir, write_dir))
+                fh.write("# command (%s): %s\n" % (name, cmd.format(counter=name, out=d)))
+            fh.write("# summarized by: python3 bench.py --summarize-counters %s %s%s\n"
+                     % (fetch_dir, write_dir, " --counters-skewed" if skewed else ""))
             fh.write("# calibration: %d-byte device copy reads FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f "
                      "KiB\n" % (CALIBRATION_BYTES, calib["FETCH_SIZE"], calib["WRITE_SIZE"]))
             fh.write("fetch_scale = %.4f\n" % factor["FETCH_SIZE"])
@@ -724,12 +732,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--counters-skewed", action="store_true",
+                    help="with --summarize-counters: the runs are of SKEWED_PMC_COMMAND")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     args = ap.parse_args()
 
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, skewed=args.counters_skewed)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)

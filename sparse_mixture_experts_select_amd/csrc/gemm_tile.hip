@@ -53,11 +53,13 @@
 // The DMA lane order fixes the LDS address, so each lane simply loads the
 // global chunk that belongs at its swizzled LDS position.
 //
-// Order.  Tiles are numbered by expert, then pairs of column tiles; within a
-// pair, the full-row tiles of the first column tile (m fastest), those of
-// the second, then the pair's tail tile.  Each XCD takes a contiguous run of
-// ceil(n/8) tile numbers (workgroup IDs are dealt to the 8 XCDs round-robin),
-// so workgroups that share a weight panel run together and share one L2.
+// Order.  Tiles are numbered by expert, then groups of two pairs of column
+// tiles (four column tiles); within a group, the full-row tiles in blocks of
+// 8 row tiles (rows fastest, then the group's columns), then the group's
+// tail tiles, one per pair.  Each XCD takes a contiguous run of ceil(n/8)
+// tile numbers (workgroup IDs are dealt to the 8 XCDs round-robin), so the
+// workgroups that run together on an XCD share A rows and weight panels in
+// one L2: an expert with many rows runs as 8 x 4 blocks of tiles.
 //
 // Last round (GEMM 2).  An XCD's tiles run in rounds of its CUs; the tiles
 // of its last, partial round may be cut into p equal K ranges (p chosen per
@@ -108,6 +110,13 @@ __device__ __forceinline__ void stage_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Tile order inside an expert (tile_geometry): groups of kGroupPairs pairs of
+// column tiles, each group's full-row tiles in blocks of kRowBlock row tiles.
+// An XCD's round of 32 tiles on an expert with many rows is then 8 row tiles
+// x 4 column tiles, which read 8 A slabs and 4 weight slabs per K step from
+// L2 (32 row tiles of one column tile would read 33).
+constexpr int kGroupPairs = 2;
+constexpr int kRowBlock = 8;
 constexpr int kMaxCpx = 32;      // CUs per XCD the schedule plans for (MI355X: 32)
 constexpr int kMaxPieces = 8;      // K pieces per cut tile (GEMM 2)
 constexpr int kPieceOverhead = 16;  // per-item cost in K steps: pipeline fill, epilogue
@@ -120,12 +129,10 @@ constexpr int kSlotFloats = kThreads * 256;  // one tile's fp32 accumulators
 // slot, pieces}, cut tiles numbered XCD by XCD.  The slots follow.
 constexpr int kHeaderFloats = 64 + 8 * 8 * kMaxCpx;
 
-// Geometry of tile t.  Tiles are numbered by expert, then pairs of column
-// tiles; within a pair, the full-row tiles of the first column tile (m
-// fastest), those of the second, then the pair's tail tile.  Per expert with
-// n_e rows: mt_n row tiles of 256 (the last one partial when more than 128
-// rows remain) per column tile, plus one tail tile per pair of column tiles
-// when 1..128 rows remain.
+// Geometry of tile t, in the order above.  Per expert with n_e rows: mt_n
+// row tiles of 256 (the last one partial when more than 128 rows remain) per
+// column tile, plus one tail tile per pair of column tiles when 1..128 rows
+// remain.
 struct TileGeo {
     int e, row0, row_end, col0;
     bool is_tail;
@@ -155,18 +162,25 @@ __device__ __forceinline__ TileGeo tile_geometry(int t, const int32_t* offsets, 
         const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
         const int per_e = mt_n * NT + tail * NTP;
         if (L < per_e) {
-            const int bs = 2 * mt_n + tail;  // tiles per pair of column tiles (the last
-                                             // pair has one column tile when NT is odd)
-            const int q = min(L / bs, NTP - 1);
-            const int r = L - q * bs;
-            const int n_in = (2 * q + 1 < NT) ? 2 : 1;
+            // group q of up to kGroupPairs pairs of column tiles (the last
+            // group may hold fewer, and its last pair one column tile when NT
+            // is odd): its full-row tiles in blocks of kRowBlock row tiles,
+            // rows fastest, then the group's tail tiles, one per pair
+            const int full_group = mt_n * 2 * kGroupPairs + tail * kGroupPairs;
+            const int q = min(L / full_group, (NTP - 1) / kGroupPairs);
+            const int r = L - q * full_group;
+            const int c_first = 2 * kGroupPairs * q;              // first column tile
+            const int n_cols = min(2 * kGroupPairs, NT - c_first);  // column tiles in the group
             g.e = e;
-            if (r < mt_n * n_in) {
-                g.col0 = (2 * q + r / mt_n) * BN;
-                g.row0 = o0 + (r % mt_n) * kBM;
+            if (r < mt_n * n_cols) {
+                const int b = r / (n_cols * kRowBlock);
+                const int w = r - b * n_cols * kRowBlock;
+                const int nb = min(kRowBlock, mt_n - b * kRowBlock);  // row tiles in the block
+                g.col0 = (c_first + w / nb) * BN;
+                g.row0 = o0 + (b * kRowBlock + w % nb) * kBM;
             } else {
                 g.is_tail = true;
-                g.col0 = 2 * q * BN;
+                g.col0 = (c_first + 2 * (r - mt_n * n_cols)) * BN;
                 g.row0 = o0 + (n_e >> 8) * kBM;
             }
             g.row_end = o0 + n_e;
