@@ -62,6 +62,8 @@ SMALL = [
     (200, 256, 512, 8, 2, torch.bfloat16),    # 256-row tiles: tail tiles only, GEMM 2 tiles cut in 2 K pieces
     (600, 512, 1024, 8, 2, torch.bfloat16),   # GEMM 2's last round cut into 4 K pieces (fixup sums them)
     (1500, 1024, 2048, 8, 2, torch.bfloat16), # GEMM 2 tiles cut into 3 K pieces, several per XCD
+    (2600, 768, 704, 2, 2, torch.bfloat16),   # 10 row tiles + a tail per expert: a partial block of
+                                              # row tiles, partial column-tile groups in both GEMMs
     (50, 100, 60, 5, 2, torch.float32),
     (200, 64, 96, 16, 4, torch.float32),
     # multi-workgroup route scan (over 4096 assignments) with wide routing
