@@ -142,9 +142,12 @@ def stage_rooflines(wl, counts, stage_ms, decode):
 
 def source_digest(workload):
     """Digest of the source of the w1/w3 kernel the workload runs (plus the
-    shared header), to tell whether committed counter figures still apply."""
+    headers it includes from the library), to tell whether committed counter
+    figures still apply."""
     h = hashlib.sha256()
-    for name in (GEMM1_KERNEL[workload][0], "common.h"):
+    src = GEMM1_KERNEL[workload][0]
+    headers = ("common.h", "tile_order.h") if src == "gemm_tile.hip" else ("common.h",)
+    for name in (src,) + headers:
         with open(os.path.join(CSRC, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

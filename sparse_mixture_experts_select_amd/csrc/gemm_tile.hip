@@ -75,6 +75,7 @@
 // row-contiguous stores.  GEMM 2 writes fp32 straight from the
 // accumulators (64-byte row segments per fragment).
 #include "common.h"
+#include "tile_order.h"
 
 #include <atomic>
 
@@ -82,7 +83,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 256;
 constexpr int kBK = 32;
 constexpr int kStageBytes = 40 * 1024;  // full tile: A 16 KiB + B 16 KiB; tail tile: A 8 + B 32
 constexpr int kBOffFull = 16 * 1024;    // B part of a stage, full tile
@@ -110,13 +110,6 @@ __device__ __forceinline__ void stage_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Tile order inside an expert (tile_geometry): groups of kGroupPairs pairs of
-// column tiles, each group's full-row tiles in blocks of kRowBlock row tiles.
-// An XCD's round of 32 tiles on an expert with many rows is then 8 row tiles
-// x 4 column tiles, which read 8 A slabs and 4 weight slabs per K step from
-// L2 (32 row tiles of one column tile would read 33).
-constexpr int kGroupPairs = 2;
-constexpr int kRowBlock = 8;
 constexpr int kMaxCpx = 32;      // CUs per XCD the schedule plans for (MI355X: 32)
 constexpr int kMaxPieces = 8;      // K pieces per cut tile (GEMM 2)
 constexpr int kPieceOverhead = 16;  // per-item cost in K steps: pipeline fill, epilogue
@@ -128,68 +121,6 @@ constexpr int kSlotFloats = kThreads * 256;  // one tile's fp32 accumulators
 // one 8-int descriptor per cut tile {row0, row_end, col0, is_tail, first
 // slot, pieces}, cut tiles numbered XCD by XCD.  The slots follow.
 constexpr int kHeaderFloats = 64 + 8 * 8 * kMaxCpx;
-
-// Geometry of tile t, in the order above.  Per expert with n_e rows: mt_n
-// row tiles of 256 (the last one partial when more than 128 rows remain) per
-// column tile, plus one tail tile per pair of column tiles when 1..128 rows
-// remain.
-struct TileGeo {
-    int e, row0, row_end, col0;
-    bool is_tail;
-};
-
-__device__ __forceinline__ int count_tiles(const int32_t* offsets, int E, int NT, int NTP) {
-    int n = 0;
-    for (int e = 0; e < E; ++e) {
-        const int n_e = offsets[e + 1] - offsets[e];
-        const int rem = n_e & (kBM - 1);
-        const int mt_n = (n_e >> 8) + (rem > 128 ? 1 : 0);
-        const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
-        n += mt_n * NT + tail * NTP;
-    }
-    return n;
-}
-
-__device__ __forceinline__ TileGeo tile_geometry(int t, const int32_t* offsets, int E, int NT,
-                                                 int NTP, int BN) {
-    TileGeo g{0, 0, 0, 0, false};
-    int L = t;
-    for (int e = 0; e < E; ++e) {
-        const int o0 = offsets[e];
-        const int n_e = offsets[e + 1] - o0;
-        const int rem = n_e & (kBM - 1);
-        const int mt_n = (n_e >> 8) + (rem > 128 ? 1 : 0);
-        const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
-        const int per_e = mt_n * NT + tail * NTP;
-        if (L < per_e) {
-            // group q of up to kGroupPairs pairs of column tiles (the last
-            // group may hold fewer, and its last pair one column tile when NT
-            // is odd): its full-row tiles in blocks of kRowBlock row tiles,
-            // rows fastest, then the group's tail tiles, one per pair
-            const int full_group = mt_n * 2 * kGroupPairs + tail * kGroupPairs;
-            const int q = min(L / full_group, (NTP - 1) / kGroupPairs);
-            const int r = L - q * full_group;
-            const int c_first = 2 * kGroupPairs * q;              // first column tile
-            const int n_cols = min(2 * kGroupPairs, NT - c_first);  // column tiles in the group
-            g.e = e;
-            if (r < mt_n * n_cols) {
-                const int b = r / (n_cols * kRowBlock);
-                const int w = r - b * n_cols * kRowBlock;
-                const int nb = min(kRowBlock, mt_n - b * kRowBlock);  // row tiles in the block
-                g.col0 = (c_first + w / nb) * BN;
-                g.row0 = o0 + (b * kRowBlock + w % nb) * kBM;
-            } else {
-                g.is_tail = true;
-                g.col0 = (c_first + 2 * (r - mt_n * n_cols)) * BN;
-                g.row0 = o0 + (n_e >> 8) * kBM;
-            }
-            g.row_end = o0 + n_e;
-            return g;
-        }
-        L -= per_e;
-    }
-    return g;
-}
 
 // Work of XCD x.  Workgroup IDs are dealt to the 8 XCDs round-robin, so XCD
 // x runs the workgroups with blockIdx % 8 == x; it gets the x-th run of
