@@ -50,21 +50,21 @@ CALIBRATION_BYTES = 1 << 30
 # Profiling commands behind the committed summaries; {out} is the rocprofv3
 # output directory that the summarizer is then pointed at.
 PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d {out} -o run -- "
-               "python3 bench.py --steps 3 --warmup 1 --stack off --skewed off --no-cpu-baseline "
-               "--calibrate-copy")
+               "python3 bench.py --steps 3 --warmup 1 --stack off --skewed off --sweep off "
+               "--no-cpu-baseline --calibrate-copy")
 # The skewed workload runs the same w1/w3 kernel as prefill, so its counters
 # come from a run of their own.
 SKEWED_PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d {out} "
                       "-o run -- python3 bench.py --workload skewed --secondary none --steps 3 "
-                      "--warmup 1 --stack off --no-cpu-baseline --calibrate-copy")
+                      "--warmup 1 --stack off --sweep off --no-cpu-baseline --calibrate-copy")
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE GRBM_COUNT"
 MFMA_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv "
                 "-d {out} -o run -- python3 bench.py --workload prefill --secondary none "
-                "--steps 3 --warmup 1 --stack off --skewed off --no-cpu-baseline")
+                "--steps 3 --warmup 1 --stack off --skewed off --sweep off --no-cpu-baseline")
 SIMDS = 256 * 4          # MI355X: 256 CUs x 4 SIMDs
 NOMINAL_CLOCK_HZ = 2.4e9  # the clock the 2.5 PFLOP/s figure assumes
 TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d {out} -o run -- "
-                 "python3 bench.py --steps 10 --warmup 2 --cpu-seconds 2")
+                 "python3 bench.py --steps 10 --warmup 2 --sweep off --cpu-seconds 2 --cpu-full none")
 
 
 def log(*a):
@@ -367,7 +367,7 @@ def run_sweep(steps, warmup, binding, inputs, torch):
                                    expert_counts=counts)
         torch.cuda.synchronize()
         active = int((counts > 0).sum().item())
-        n = max(steps, 5)
+        n = max(steps, 3)
         for _ in range(warmup):
             binding.moe_ffn_forward(x, w["w_router"], w["w1"], w["w3"], w["w2"], wl.k, out=out)
         torch.cuda.synchronize()
@@ -414,8 +414,51 @@ def roofline(res, bound):
             "traffic": committed_traffic(res["workload"])}
 
 
-def cpu_baseline(res, seconds, inputs):
-    """The fp64 oracle on the host cores on a bounded sample of the workload."""
+def _host_facts():
+    cpu_model, ram_gb = "unknown", None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as fh:
+            for line in fh:
+                if line.startswith("MemTotal"):
+                    ram_gb = round(int(line.split()[1]) / 1024 ** 2, 1)
+                    break
+    except OSError:
+        pass
+    return cpu_model, ram_gb
+
+
+def _oracle_full_pass(name, inputs, torch):
+    """One timed pass of the oracle over every token of a workload (the
+    whole layer per token, fp64, OpenMP over tokens); inputs are drawn on
+    the GPU exactly as the GPU runs see them, then copied to the host."""
+    import oracle
+    inp = inputs.workload_inputs(name, "cuda")
+    host = {n: inputs.host_array(inp[n]) for n in ("x", "w_router", "w1", "w3", "w2")}
+    bias = None if inp["bias"] is None else inputs.host_array(inp["bias"])
+    wl = inputs.WORKLOADS[name]
+    del inp
+    torch.cuda.empty_cache()
+    t0 = time.perf_counter()
+    oracle.moe_tokens(host["x"], host["w_router"], host["w1"], host["w3"], host["w2"], wl.k,
+                      bias=bias)
+    el = time.perf_counter() - t0
+    log("[bench] oracle, full %s workload (%d tokens): %.2f s" % (name, wl.T, el))
+    return {"tokens": wl.T, "seconds": round(el, 3), "tokens_per_s": round(wl.T / el, 3)}
+
+
+def cpu_baseline(res, seconds, inputs, torch, full=("tiny", "prefill")):
+    """The fp64 oracle on the host cores: the primary workload's tokens
+    repeated for about `seconds` (its figure is `value`), then one pass over
+    every token of each workload in `full`, each timed in full.  The skewed
+    and stack workloads would take minutes (about 150 s and 600 s on 16
+    cores); their times are extrapolated from the per-token cost, which is
+    the same in every workload at these shapes (each token runs k experts of
+    one shape)."""
     import numpy as np
 
     import oracle
@@ -434,35 +477,22 @@ def cpu_baseline(res, seconds, inputs):
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 50:
             break
+    del host
     tok_s = reps * n_tok / el
-    cpu_model, ram_gb = "unknown", None
-    try:
-        with open("/proc/cpuinfo") as fh:
-            for line in fh:
-                if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
-        with open("/proc/meminfo") as fh:
-            for line in fh:
-                if line.startswith("MemTotal"):
-                    ram_gb = round(int(line.split()[1]) / 1024 ** 2, 1)
-                    break
-    except OSError:
-        pass
-    # Every token runs k experts of the same shape, so the oracle's cost per
-    # token is the same in every workload; full-size figures are that times
-    # the token count (extrapolated, not timed).
+    cpu_model, ram_gb = _host_facts()
     per_tok = el / (reps * n_tok)
-    full = {}
-    for name in ("decode", "prefill", "skewed", "stack"):
+    timed = {name: _oracle_full_pass(name, inputs, torch) for name in full}
+    extrap = {}
+    for name in ("skewed", "stack"):
         w = inputs.WORKLOADS[name]
-        full[name] = round(per_tok * w.T * getattr(w, "layers", 1), 1)
+        extrap[name] = round(per_tok * w.T * getattr(w, "layers", 1), 1)
     return {"value": round(tok_s, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle", "cpu_model": cpu_model, "ram_gb": ram_gb, "nproc": os.cpu_count(),
-            "sample": "%s workload, tokens 0..%d (full layer per token in fp64), %d passes, %.1f s"
-                      % (wl.name, n_tok - 1, reps, el),
+            "sample": "%s workload, tokens 0..%d (the whole workload; full layer per token in "
+                      "fp64), %d passes, %.1f s" % (wl.name, n_tok - 1, reps, el),
             "seconds_per_token_layer": round(per_tok, 5),
-            "extrapolated_full_workload_seconds": full}
+            "timed_full_workloads": timed,
+            "extrapolated_full_workload_seconds": extrap}
 
 
 def device_facts(torch):
@@ -729,8 +759,13 @@ def main():
                     help="also run the skewed-routing workload (T=16384, biased router)")
     ap.add_argument("--stack", default="on", choices=["on", "off"],
                     help="also time the 32-block stack (90 GB of weights resident)")
-    ap.add_argument("--sweep", action="store_true",
+    ap.add_argument("--sweep", default="on", choices=["on", "off"],
                     help="also time the layer over T = 1 .. 16384 (prefill weights)")
+    ap.add_argument("--sweep-steps", type=int, default=5,
+                    help="timed steps per batch size in the sweep")
+    ap.add_argument("--cpu-full", nargs="+", default=["tiny", "prefill"],
+                    choices=["tiny", "decode", "prefill", "none"],
+                    help="workloads the oracle is also timed on in full")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -825,11 +860,11 @@ def main():
         rec["secondary"] = side_workload(args.secondary)
     if args.skewed == "on" and args.workload != "skewed" and args.secondary != "skewed":
         rec["skewed"] = side_workload("skewed")
-    if args.sweep:
+    if args.sweep == "on":
         prim_inp = prim.pop("inp")
         del prim_inp
         torch.cuda.empty_cache()
-        rec["sweep"] = run_sweep(args.steps, args.warmup, binding, inputs, torch)
+        rec["sweep"] = run_sweep(args.sweep_steps, min(args.warmup, 2), binding, inputs, torch)
         torch.cuda.empty_cache()
         prim["inp"] = inputs.workload_inputs(args.workload, "cuda")
     if args.stack == "on":
@@ -853,7 +888,8 @@ def main():
     if args.no_cpu_baseline:
         rec["cpu_baseline"] = None
     else:
-        rec["cpu_baseline"] = cpu_baseline(prim, args.cpu_seconds, inputs)
+        rec["cpu_baseline"] = cpu_baseline(prim, args.cpu_seconds, inputs, torch,
+                                           full=tuple(w for w in args.cpu_full if w != "none"))
     print(json.dumps(rec), flush=True)
 
 

@@ -31,8 +31,8 @@
  *       T == 0                                   -> MOE_OK, nothing enqueued
  *       NULL tensor pointer with T > 0, or d, f, E, k < 1, or T < 0
  *                                                -> MOE_ERR_INVALID_ARG
- *       k > E, E > 64, k > 8, d or f not a multiple of 64 (bf16) or of 4
- *       (fp32), a pointer not 16-byte aligned    -> MOE_ERR_UNSUPPORTED
+ *       k > E, E > 64, d or f not a multiple of 64 (bf16) or of 4 (fp32),
+ *       a pointer not 16-byte aligned            -> MOE_ERR_UNSUPPORTED
  *     A failing HIP call returns MOE_ERR_HIP; a failed workspace allocation
  *     MOE_ERR_OUT_OF_MEMORY.  moe_ffn_last_error() then describes it.
  *   - Inputs must be finite; non-finite values give undefined results.

@@ -155,7 +155,6 @@ moe_status_t check_sizes(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, 
                     (long long)T, (long long)d, (long long)f, (long long)E, (long long)k);
     if (k > E) return fail(MOE_ERR_UNSUPPORTED, "k=%lld exceeds E=%lld", (long long)k, (long long)E);
     if (E > 64) return fail(MOE_ERR_UNSUPPORTED, "E=%lld exceeds 64", (long long)E);
-    if (k > 8) return fail(MOE_ERR_UNSUPPORTED, "k=%lld exceeds 8", (long long)k);
     const int64_t mult = dtype == MOE_DTYPE_BF16 ? 64 : 4;
     if (d % mult != 0 || f % mult != 0)
         return fail(MOE_ERR_UNSUPPORTED, "d=%lld and f=%lld must be multiples of %lld", (long long)d,

@@ -18,7 +18,7 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxPicks = 8;    // k <= 8 (checked by the entry points)
+constexpr int kPickBatch = 8;   // picks whose rows and gates are loaded together
 constexpr int kMaxSlices = 16;  // K-slice partials of y (the host plans at most 16)
 
 template <typename T> struct Io;
@@ -77,13 +77,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     constexpr int U = 4;
     const int d4 = d / 4;
     for (int t = blockIdx.x; t < Tn; t += gridDim.x) {
-        int rows[kMaxPicks];
-        float g[kMaxPicks];
-#pragma unroll
-        for (int j = 0; j < kMaxPicks; ++j) {
-            rows[j] = j < k ? slot_row[(size_t)t * k + j] : 0;
-            g[j] = j < k ? gates[(size_t)t * k + j] : 0.0f;
-        }
         for (int c0 = threadIdx.x; c0 < d4; c0 += 256 * U) {
             float4 acc[U];
 #pragma unroll
@@ -99,16 +92,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                     if (c < d4) Io<T>::load4(residual, (size_t)t * d4 + c, rv[u]);
                 }
             }
+            // picks in batches of kPickBatch (one batch for k <= 8), in slot
+            // order
+            for (int j0 = 0; j0 < k; j0 += kPickBatch) {
+                int rows[kPickBatch];
+                float g[kPickBatch];
 #pragma unroll
-            for (int j = 0; j < kMaxPicks; ++j) {
-                if (j >= k) break;
-                const float4* yr = reinterpret_cast<const float4*>(y + (size_t)rows[j] * d);
+                for (int j = 0; j < kPickBatch; ++j) {
+                    rows[j] = j0 + j < k ? slot_row[(size_t)t * k + j0 + j] : 0;
+                    g[j] = j0 + j < k ? gates[(size_t)t * k + j0 + j] : 0.0f;
+                }
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + 256 * u;
-                    const float4 sv = c < d4 ? yr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-                    acc[u].x += g[j] * sv.x; acc[u].y += g[j] * sv.y;
-                    acc[u].z += g[j] * sv.z; acc[u].w += g[j] * sv.w;
+                for (int j = 0; j < kPickBatch; ++j) {
+                    if (j0 + j >= k) break;
+                    const float4* yr = reinterpret_cast<const float4*>(y + (size_t)rows[j] * d);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int c = c0 + 256 * u;
+                        const float4 sv = c < d4 ? yr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+                        acc[u].x += g[j] * sv.x; acc[u].y += g[j] * sv.y;
+                        acc[u].z += g[j] * sv.z; acc[u].w += g[j] * sv.w;
+                    }
                 }
             }
 #pragma unroll

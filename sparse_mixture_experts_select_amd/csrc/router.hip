@@ -15,7 +15,9 @@
 // element.  The TPW x E partial logits of a lane are summed across the lanes
 // of a wave with a halving butterfly (each exchange step sends half as many
 // values as the one before), then across the 4 waves in LDS in a fixed
-// order, and lane tt of wave 0 selects and normalises token tt.
+// order; then one lane of wave 0 per (token, expert) finds that expert's
+// rank among the token's logits, and the lanes of ranks 0..k-1 write the
+// picks and their softmax weights (any k <= E <= 64).
 //
 // Logits stay fp32 (products of bf16 inputs are exact in fp32, sums are
 // fp32).  Ties break toward the lower expert index; the picks are stored by
@@ -36,7 +38,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxK = 8;
 // Fused RMSNorm: the first kNormCache 16-byte slices of each of a lane's rows
 // stay in registers between the two passes (all of a row up to d = 4096 in
 // bf16), so the second pass reloads only what lies past them.
@@ -251,60 +252,51 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(
     wave_sum_split<NV>(v, lane);
     if ((lane & ((1 << SHIFT) - 1)) == 0) (&part[wave][0][0])[lane >> SHIFT] = v[0];
     __syncthreads();
-    if (wave != 0 || lane >= TPW) return;
-
-    const int tt = lane;
+    // Selection: lane (tt, e) of wave 0 holds token tt's logit of expert e
+    // (TPW * EMAX <= 64 lanes).  Its stable rank -- the number of experts
+    // before it in the order (logit descending, index ascending) -- is its
+    // slot: rank j is what the j-th round of an argmax with strict '>' over
+    // ascending indices would pick, so the k picks are the ranks 0..k-1 with
+    // ties kept by the lower index, for any k <= E.
+    static_assert(TPW * EMAX <= 64, "one lane of wave 0 per (token, expert)");
+    __shared__ float logit[TPW][EMAX];
+    __shared__ float pexp[TPW][EMAX];
+    const int tt = lane / EMAX;
+    const int e = lane % EMAX;
     const int t = t0 + tt;
-    if (t >= T_) return;
-    float l[EMAX];
+    const bool mine = wave == 0 && lane < TPW * EMAX && e < E && t < T_;
+    float l = 0.0f;
+    if (mine) {
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) {
-        float v = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) v += part[w][tt][e];
-        if (bias != nullptr && e < E) v += bias[e];
-        l[e] = v;
+        for (int w = 0; w < kWaves; ++w) l += part[w][tt][e];
+        if (bias != nullptr) l += bias[e];
+        logit[tt][e] = l;
     }
-    // k rounds of argmax over the experts not yet taken; strict '>' in
-    // ascending expert order keeps the lowest index on ties.
-    uint64_t taken = 0;
-    int sel[kMaxK];
-    float sv[kMaxK];
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        if (j < k) {
-            int best = -1;
-            float bv = 0.0f;
-#pragma unroll
-            for (int e = 0; e < EMAX; ++e) {
-                const bool free_e = (e < E) && !((taken >> e) & 1ull);
-                if (free_e && (best < 0 || l[e] > bv)) {
-                    best = e;
-                    bv = l[e];
-                }
-            }
-            taken |= 1ull << best;
-            sel[j] = best;
-            sv[j] = bv;
+    __syncthreads();
+    int rank = E;
+    float p = 0.0f;
+    if (mine) {
+        rank = 0;
+        float lmax = logit[tt][0];
+        for (int o = 0; o < E; ++o) {
+            const float lo = logit[tt][o];
+            rank += (lo > l || (lo == l && o < e)) ? 1 : 0;
+            lmax = fmaxf(lmax, lo);
+        }
+        // softmax over the k kept logits, max-subtracted (the rank-0 logit)
+        if (rank < k) {
+            p = expf(l - lmax);
+            pexp[tt][rank] = p;
         }
     }
-    // softmax over the k kept logits; sv[0] is the largest.
-    float p[kMaxK];
-    float z = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        if (j < k) {
-            p[j] = expf(sv[j] - sv[0]);
-            z += p[j];
-        }
-    }
-    const float rz = 1.0f / z;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-        if (j < k) {
-            ids[(size_t)t * k + j] = sel[j];
-            gates[(size_t)t * k + j] = p[j] * rz;
-        }
+    __syncthreads();
+    if (mine && rank < k) {
+        // the normaliser summed in slot order, so every lane of the token
+        // forms the same value
+        float z = 0.0f;
+        for (int j = 0; j < k; ++j) z += pexp[tt][j];
+        ids[(size_t)t * k + rank] = e;
+        gates[(size_t)t * k + rank] = p * (1.0f / z);
     }
 }
 

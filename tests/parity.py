@@ -199,9 +199,33 @@ def host_inputs(inp):
             if kk in ("x", "w_router", "w1", "w3", "w2")}
 
 
+def segment_sample_tokens(g, seed, step=128):
+    """Tokens whose grouped rows reach every row block of every expert
+    segment: each expert's rows [offsets[e], offsets[e+1]) are cut into
+    blocks of ``step`` rows from the segment's start, and each block gives
+    its first row, its last row and one random row.  With step dividing the
+    GEMM tiles' row heights, every row tile of every expert (full, partial,
+    tail) holds checked rows, and a checked row is compared over all its
+    columns, so every tile the GEMMs run -- whole, cut into K pieces or a
+    tail -- is covered.  Picked from the GPU's own offsets and row_token."""
+    offsets = to_np(g["offsets"])
+    row_token = to_np(g["row_token"])
+    rng = np.random.default_rng(seed)
+    rows = []
+    for e in range(len(offsets) - 1):
+        o0, o1 = int(offsets[e]), int(offsets[e + 1])
+        for b in range(o0, o1, step):
+            hi = min(b + step, o1)
+            rows += [b, hi - 1, int(rng.integers(b, hi))]
+    if not rows:
+        return np.zeros(0, np.int64)
+    return np.unique(row_token[np.asarray(rows, np.int64)]).astype(np.int64)
+
+
 def full_check(inp, k, tokens=None, want_h=True, want_y=True, label=""):
     """Run the GPU layer and check routing on every token and outputs on
-    ``tokens`` (all tokens when None).  Returns a summary dict."""
+    ``tokens`` (all tokens when None; a callable is given the GPU results
+    and returns the tokens).  Returns a summary dict."""
     x = inp["x"]
     g = run_gpu(inp, k, want_h=want_h, want_y=want_y)
     host = host_inputs(inp)
@@ -209,7 +233,12 @@ def full_check(inp, k, tokens=None, want_h=True, want_y=True, label=""):
     logits, o_ids, _ = oracle.route(host["x"], host["w_router"], k, bias=bias)
     exempt = check_routing(g, logits, o_ids, k)
     T = x.shape[0]
-    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    if tokens is None:
+        tok = np.arange(T)
+    elif callable(tokens):
+        tok = np.asarray(tokens(g))
+    else:
+        tok = np.asarray(tokens)
     errs = check_outputs(g, host, tok, logits, k, x.dtype)
     return {"label": label, "near_ties": int(exempt.sum()), "err_out": errs[0],
-            "err_h": errs[1], "err_y": errs[2], "gpu": g}
+            "err_h": errs[1], "err_y": errs[2], "gpu": g, "tokens": tok}

@@ -72,7 +72,7 @@ def test_zero_tokens_is_a_no_op(binding):
     (dict(out=0), 1),
     (dict(T=-1), 1),
     (dict(d=0), 1), (dict(f=0), 1), (dict(E=0), 1), (dict(k=0), 1),
-    (dict(k=9, E=16), 2),             # k > 8
+    (dict(k=17, E=16), 2),            # k > E
     (dict(k=3, E=2), 2),              # k > E
     (dict(E=65), 2),                  # E > 64
     (dict(d=96), 2),                  # d not a multiple of 64 (bf16)
