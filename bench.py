@@ -448,7 +448,7 @@ def _oracle_full_pass(name, inputs, torch):
                       bias=bias)
     el = time.perf_counter() - t0
     log("[bench] oracle, full %s workload (%d tokens): %.2f s" % (name, wl.T, el))
-    return {"tokens": wl.T, "seconds": round(el, 3), "tokens_per_s": round(wl.T / el, 3)}
+    return {"tokens": wl.T, "seconds": round(el, 6), "tokens_per_s": round(wl.T / el, 3)}
 
 
 def cpu_baseline(res, seconds, inputs, torch, full=("tiny", "prefill")):
@@ -529,6 +529,50 @@ def read_probe(torch, binding, nbytes=4 << 30, reps=3):
     gbs = nbytes / (best[0] * 1e-3) / 1e9
     log("[bench] read probe: %.1f GB/s (%d bytes, %d workgroups)" % (gbs, nbytes, best[1]))
     return gbs, best[1]
+
+
+def mfma_probe(torch, binding, ms_target=150.0):
+    """Measured bf16 matrix-core rate of this GPU under a dense MFMA stream
+    on random operands (the library's MFMA probe: the tile GEMMs' per-wave
+    8 x 8 fragment shape, one workgroup of 4 waves per CU, no memory
+    traffic), beside the 2.5 PFLOP/s datasheet figure, which assumes 2.4 GHz.
+    Run for about ms_target milliseconds, long enough for the clock to
+    settle at what the power limit allows; best of two runs, with the clock
+    the probe recorded (shader cycles over 100 MHz real-time ticks)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ops = torch.randn(4 << 20, dtype=torch.float32, device="cuda").to(torch.bfloat16)  # 8 MiB
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
+
+    def timed(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        binding.moe_mfma_probe(ops, iters, cus, sink, clocks)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    short = 2000
+    per_iter = timed(short) / short
+    iters = int(min(max(ms_target / per_iter, short), 1 << 24))
+    best = None
+    for _ in range(2):
+        ms = timed(iters)
+        ck = clocks.cpu().numpy().reshape(cus, 2).astype(float)
+        ghz = ck[:, 0].sum() / ck[:, 1].sum() * 0.1
+        if best is None or ms < best[0]:
+            best = (ms, ghz)
+    flops = cus * 4.0 * iters * 128 * 16384
+    tflops = flops / (best[0] * 1e-3) / 1e12
+    log("[bench] MFMA probe: %.1f TFLOP/s (%.3f of %.0f), clock %.3f GHz, %d x %d iterations"
+        % (tflops, tflops / MFMA_BF16_PEAK_TFLOPS, MFMA_BF16_PEAK_TFLOPS, best[1], cus, iters))
+    del ops
+    torch.cuda.empty_cache()
+    return {"what": "v_mfma_f32_16x16x32_bf16 on random bf16 operands, no memory traffic, one "
+                    "workgroup of 4 waves per CU, 8 x 8 fragments per wave (moe_mfma_probe), "
+                    "%.0f ms" % best[0],
+            "tflops": round(tflops, 1), "frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "clock_ghz": round(best[1], 3)}
 
 
 def calibrate_copy(torch, nbytes=CALIBRATION_BYTES, reps=3):
@@ -876,6 +920,14 @@ def main():
         prim["inp"] = inputs.workload_inputs(args.workload, "cuda")
     if args.calibrate_copy:
         calibrate_copy(torch)
+    rec["mfma_probe"] = mfma_probe(torch, binding)
+    for key in ("secondary", "skewed", "stack"):
+        rl = rec.get(key, {}).get("roofline")
+        if rl and rl["bound"] == "mfma":
+            rl["frac_of_mfma_probe"] = round(rl["achieved"] / rec["mfma_probe"]["tflops"], 4)
+    if bound == "mfma":
+        rec["roofline"]["frac_of_mfma_probe"] = round(
+            rec["roofline"]["achieved"] / rec["mfma_probe"]["tflops"], 4)
     if bound == "hbm":
         probe, blocks = read_probe(torch, binding)
         rec["read_probe"] = {

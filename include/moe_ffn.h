@@ -184,6 +184,24 @@ const char *moe_ffn_stage_name(int32_t stage);
 moe_status_t moe_hbm_read_probe(const void *buf, size_t bytes, int32_t blocks, uint32_t *sink,
                                 void *stream);
 
+/*
+ * Measurement aid, not part of the layer: bf16 matrix-core work with no
+ * memory traffic, the ceiling the MFMA-bound grouped GEMMs are compared with
+ * beside the 2.5 PFLOP/s datasheet figure (that figure assumes 2.4 GHz; a
+ * dense MFMA stream on random data runs at the clock the part's power limit
+ * allows).  `blocks` workgroups (1..65536; one per compute unit measures the
+ * whole chip) of 4 wavefronts; each wavefront issues iters (1..2^24) x 128
+ * v_mfma_f32_16x16x32_bf16 (16384 flops each) on operand fragments read once
+ * from `operands` (device, 16-byte aligned, operand_bytes >= 16 KiB and a
+ * multiple of 16; random bf16 data gives realistic power).  *sink (a device
+ * uint32) receives an XOR fold of the results, which keeps them live.
+ * clocks (device, optional): per workgroup two uint64, the shader-clock
+ * cycles and the 100 MHz real-time ticks of its MFMA loop.  Enqueued on
+ * `stream`.
+ */
+moe_status_t moe_mfma_probe(const void *operands, size_t operand_bytes, int32_t iters,
+                            int32_t blocks, uint32_t *sink, uint64_t *clocks, void *stream);
+
 /* Text describing the last non-OK status returned on this host thread. */
 const char *moe_ffn_last_error(void);
 

@@ -85,6 +85,8 @@ lib.moe_ffn_version.argtypes = []
 lib.moe_ffn_version.restype = ctypes.c_char_p
 lib.moe_hbm_read_probe.argtypes = [_P, ctypes.c_size_t, ctypes.c_int32, _P, _P]
 lib.moe_hbm_read_probe.restype = ctypes.c_int
+lib.moe_mfma_probe.argtypes = [_P, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+lib.moe_mfma_probe.restype = ctypes.c_int
 
 
 class MoeError(RuntimeError):
@@ -226,6 +228,20 @@ def moe_hbm_read_probe(buf, blocks, sink, stream=None) -> None:
         raise ValueError("buf must be a contiguous GPU tensor and sink an int32 GPU tensor")
     nbytes = buf.numel() * buf.element_size()
     _check(lib.moe_hbm_read_probe(_ptr(buf), nbytes, int(blocks), _ptr(sink), _stream(stream)))
+
+
+def moe_mfma_probe(ops, iters, blocks, sink, clocks=None, stream=None) -> None:
+    """Enqueue the MFMA probe (see the header) on the contiguous GPU tensor
+    ``ops``; ``sink`` is a one-element int32 GPU tensor, ``clocks`` an
+    optional int64 GPU tensor of 2 * blocks elements."""
+    if not ops.is_cuda or not ops.is_contiguous() or not sink.is_cuda or sink.dtype != torch.int32:
+        raise ValueError("ops must be a contiguous GPU tensor and sink an int32 GPU tensor")
+    if clocks is not None and (not clocks.is_cuda or clocks.dtype != torch.int64
+                               or clocks.numel() < 2 * blocks):
+        raise ValueError("clocks must be an int64 GPU tensor of at least 2 * blocks elements")
+    nbytes = ops.numel() * ops.element_size()
+    _check(lib.moe_mfma_probe(_ptr(ops), nbytes, int(iters), int(blocks), _ptr(sink), _ptr(clocks),
+                              _stream(stream)))
 
 
 def moe_ffn_last_error() -> str:

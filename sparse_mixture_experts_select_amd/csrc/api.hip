@@ -505,6 +505,21 @@ moe_status_t moe_hbm_read_probe(const void* buf, size_t bytes, int32_t blocks, u
     return MOE_OK;
 }
 
-const char* moe_ffn_version(void) { return "0.1.0"; }
+moe_status_t moe_mfma_probe(const void* operands, size_t operand_bytes, int32_t iters,
+                            int32_t blocks, uint32_t* sink, uint64_t* clocks, void* stream) {
+    if (!operands || !sink) return fail(MOE_ERR_INVALID_ARG, "a pointer is NULL");
+    if (!aligned16(operands) || operand_bytes % 16 != 0 || operand_bytes < 16 * 1024)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "operands must be 16-byte aligned, at least 16 KiB and a multiple of 16 bytes");
+    if (iters < 1 || iters > (1 << 24)) return fail(MOE_ERR_INVALID_ARG, "iters must be in [1, 2^24]");
+    if (blocks < 1 || blocks > 65536) return fail(MOE_ERR_INVALID_ARG, "blocks must be in [1, 65536]");
+    LAUNCH(launch_mfma_probe(operands, operand_bytes, iters, blocks, sink,
+                             reinterpret_cast<unsigned long long*>(clocks),
+                             reinterpret_cast<hipStream_t>(stream)),
+           "mfma_probe");
+    return MOE_OK;
+}
+
+const char* moe_ffn_version(void) { return "0.2.0"; }
 
 }  // extern "C"

@@ -105,6 +105,12 @@ hipError_t launch_rmsnorm(int dtype, const void* h, void* x, int T, int d, float
 hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink,
                              hipStream_t stream);
 
+// bf16 MFMA work on operands read once from ops (bytes, a multiple of 16):
+// `blocks` workgroups of 4 waves, each wave iters x 128 v_mfma_f32_16x16x32_bf16.
+// clocks (optional): per workgroup {shader cycles, 100 MHz ticks}.
+hipError_t launch_mfma_probe(const void* ops, size_t bytes, int iters, int blocks, uint32_t* sink,
+                             unsigned long long* clocks, hipStream_t stream);
+
 // Tile shapes of the bf16 grouped GEMMs, chosen by the host per call.
 enum GemmVariant { GEMM_LARGE_M = 0, GEMM_SMALL_M = 1, GEMM_STREAM = 2, GEMM_TILE256 = 3 };
 int gemm_bm(int variant);      // rows per tile

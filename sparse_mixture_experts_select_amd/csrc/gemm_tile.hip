@@ -170,9 +170,9 @@ __device__ __forceinline__ int2 xcd_bases(int n_tiles, int x, int cpx, int KT, i
     return b;
 }
 
-// ---- epilogue of one tile: lane holds rows 4*lgrp + r (r = 0..3) of column
-// lrow of each fragment.  st0 and st1 are two LDS arrays of at least 32 KiB
-// (GEMM 1 stages h through them).
+// ---- GEMM 1 epilogue of one tile: lane holds rows 4*lgrp + r (r = 0..3) of
+// column lrow of each fragment.  st0 and st1 are two LDS arrays of at least
+// 32 KiB that h is staged through.
 template <bool DUAL>
 __device__ __forceinline__ void tile_epilogue(const floatx4 (&acc)[8][8], const TileGeo& geo,
                                               void* __restrict__ C, int R, int N, int kb,
@@ -242,22 +242,6 @@ __device__ __forceinline__ void tile_epilogue(const floatx4 (&acc)[8][8], const 
                         *reinterpret_cast<const uint4*>(hs_r + rr * 128 + ((ch ^ (rr & 15)) << 3));
             }
         }
-    } else {
-        float* y = reinterpret_cast<float*>(C);
-        const int rbase = row0 + (is_tail ? 0 : wm * 128);
-        const int cbase = col0 + (is_tail ? wm * BN : 0) + wn * 128;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int grow = rbase + 16 * m + 4 * lgrp + r;
-                if (grow >= row_end) continue;
-#pragma unroll
-                for (int n = 0; n < 8; ++n) {
-                    const int gc = cbase + 16 * n + lrow;
-                    if (gc < N) y[(size_t)grow * N + gc] = acc[m][n][r];
-                }
-            }
     }
 }
 
@@ -307,6 +291,11 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     const TileGeo geo = tile_geometry(t, offsets, E, NT, NTP, BN);
     const int e = geo.e, row0 = geo.row0, row_end = geo.row_end, col0 = geo.col0;
     const bool is_tail = geo.is_tail;
+    // A K piece's partial-sum slot and cut-tile number, found here, where
+    // they cost two wave-uniform scalars (after the K loop the search would
+    // compete with the accumulators for registers).
+    int2 piece_bases = make_int2(0, 0);
+    if (!DUAL && piece >= 0) piece_bases = xcd_bases(n_tiles, xcd, cpx, KT, max_pieces);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -541,16 +530,26 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     // No load may still be writing LDS when the stages are reused below.
     MOE_WAIT_VM(0);
 
-    if (DUAL || piece < 0) {
+    if (DUAL) {
         tile_epilogue<DUAL>(acc, geo, C, R, N, kb, st0, st1);
+        return;
+    }
+    // GEMM 2: one store loop for both cases, so the accumulators go out
+    // in one pass with no branch between two store paths.  A whole tile
+    // writes fp32 y; a K piece writes its fp32 partial sums to its slot,
+    // laid out as the tile itself, row-major: 256 rows x 256 columns, or
+    // 128 rows x 512 columns (both column tiles) for a tail tile.
+    float* dst;
+    int stride, rlim, clim;
+    if (piece < 0) {
+        dst = reinterpret_cast<float*>(C) + (size_t)row0 * N + col0;
+        stride = N;
+        rlim = row_end - row0;
+        clim = N - col0;
     } else {
-        // a K piece: its fp32 accumulators go to a partial-sum slot laid out
-        // as the tile itself, row-major: 256 rows x 256 columns, or 128 rows
-        // x 512 columns (both column tiles) for a tail tile
-        const int2 bases = xcd_bases(n_tiles, xcd, cpx, KT, max_pieces);
-        const int first_slot = bases.x + rt * sc.p;
+        const int first_slot = piece_bases.x + rt * sc.p;
         if (piece == 0 && threadIdx.x == 0) {
-            int* desc = reinterpret_cast<int*>(partials) + 64 + 8 * (bases.y + rt);
+            int* desc = reinterpret_cast<int*>(partials) + 64 + 8 * (piece_bases.y + rt);
             desc[0] = row0;
             desc[1] = row_end;
             desc[2] = col0;
@@ -558,21 +557,30 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
             desc[4] = first_slot;
             desc[5] = sc.p;
         }
-        float* dst = partials + kHeaderFloats + (size_t)(first_slot + piece) * kSlotFloats;
-        const int lane = threadIdx.x & 63;
-        const int wave = threadIdx.x >> 6;
-        const int wm = wave >> 1, wn = wave & 1, lrow = lane & 15, lgrp = lane >> 4;
-        const int width = is_tail ? 512 : 256;
-        const int rbase = (is_tail ? 0 : wm * 128) + 4 * lgrp;
-        const int cbase = (is_tail ? wm * 256 : 0) + wn * 128 + lrow;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int n = 0; n < 8; ++n)
-                    dst[(rbase + 16 * m + r) * width + cbase + 16 * n] = acc[m][n][r];
+        dst = partials + kHeaderFloats + (size_t)(first_slot + piece) * kSlotFloats;
+        stride = is_tail ? 512 : 256;
+        rlim = 1 << 30;
+        clim = 1 << 30;
     }
+    // The lane terms are formed afresh here (wave index as a scalar, lane
+    // from mbcnt) rather than reused from before the K loop, where keeping
+    // them would cost registers across it.
+    const int ewave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int rbase = (is_tail ? 0 : (ewave >> 1) * 128) + 4 * (elane >> 4);
+    const int cbase = (is_tail ? (ewave >> 1) * BN : 0) + (ewave & 1) * 128 + (elane & 15);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = rbase + 16 * m + r;
+            if (row >= rlim) continue;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const int col = cbase + 16 * n;
+                if (col < clim) dst[(size_t)row * stride + col] = acc[m][n][r];
+            }
+        }
 }
 
 // GEMM 2's tiles cut into K pieces: sum the pieces' partial sums in piece

@@ -1,10 +1,23 @@
-// probe.hip -- a plain streaming read of a device buffer, the measured
-// ceiling that the weight-streaming (HBM-bound) kernels are compared with
-// beside the 8 TB/s datasheet figure.  Not part of the layer.
+// probe.hip -- measurement aids, not part of the layer:
 //
-// Each thread reads 16-byte vectors in a grid-stride loop, four in flight per
-// iteration, and folds them with XOR so no load is dead; one atomic per wave
-// writes the fold to `sink` (its value has no meaning).
+// read_probe_kernel: a plain streaming read of a device buffer, the measured
+// ceiling that the weight-streaming (HBM-bound) kernels are compared with
+// beside the 8 TB/s datasheet figure.  Each thread reads 16-byte vectors in a
+// grid-stride loop, four in flight per iteration, and folds them with XOR so
+// no load is dead; one atomic per wave writes the fold to `sink` (its value
+// has no meaning).
+//
+// mfma_probe_kernel: bf16 matrix-core work with no memory traffic, the
+// measured ceiling that the MFMA-bound tile GEMMs are compared with beside
+// the 2.5 PFLOP/s datasheet figure (which assumes 2.4 GHz; under a dense
+// MFMA stream on random data the part holds a lower clock).  Each of the
+// four waves of a workgroup runs the tile GEMMs' per-wave shape -- 8 x 8
+// fragments of v_mfma_f32_16x16x32_bf16, 256 fp32 accumulators -- on 8 A and
+// 8 B operand fragments read once from `ops` (random data, so operand bits
+// toggle from one MFMA to the next as in a real product), paired differently
+// in the two halves of an iteration; a 96 KiB LDS reservation keeps one
+// workgroup per CU, as in the tile GEMMs.  Optionally records each workgroup's shader-clock cycles and
+// 100 MHz real-time ticks, which give the clock held under that load.
 #include "common.h"
 
 namespace moe {
@@ -26,7 +39,68 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
     if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
 }
 
+constexpr int kProbeHold = 24 * 1024;  // uint32 words of LDS reserved per workgroup
+
+__global__ __launch_bounds__(256, 1) void mfma_probe_kernel(const uint4* __restrict__ ops, size_t n16,
+                                                            int iters, uint32_t* __restrict__ sink,
+                                                            unsigned long long* __restrict__ clocks) {
+    __shared__ uint32_t hold[kProbeHold];
+    const size_t base = ((size_t)blockIdx.x * 256 + threadIdx.x) * 16;
+    bf16x8 a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = __builtin_bit_cast(bf16x8, ops[(base + i) % n16]);
+        b[i] = __builtin_bit_cast(bf16x8, ops[(base + 8 + i) % n16]);
+    }
+    floatx4 acc[8][8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    hold[threadIdx.x] = 0u;
+    const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    // Each MFMA accumulates in place in its AGPRs.  (Written as inline asm:
+    // with loop-invariant operands the compiler otherwise rotates the
+    // accumulators through other registers every iteration, which is not
+    // the tile GEMMs' instruction stream.)
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                                 : "+a"(acc[m][n])
+                                 : "v"(a[(m + h) & 7]), "v"(b[(n + 3 * h) & 7]));
+    }
+    // let the last MFMAs retire before their accumulators are read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
+    uint32_t f = hold[threadIdx.x];  // 0: only keeps the LDS reservation
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+            f ^= __float_as_uint(acc[m][n][0] + acc[m][n][1] + acc[m][n][2] + acc[m][n][3]);
+    for (int off = 32; off >= 1; off >>= 1) f ^= __shfl_xor(f, off, 64);
+    if ((threadIdx.x & 63) == 0) atomicXor(sink, f);
+    if (clocks != nullptr && threadIdx.x == 0) {
+        clocks[2 * blockIdx.x] = c1 - c0;
+        clocks[2 * blockIdx.x + 1] = t1 - t0;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(const void* ops, size_t bytes, int iters, int blocks, uint32_t* sink,
+                             unsigned long long* clocks, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(ops), bytes / 16, iters, sink, clocks);
+    return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink,
                              hipStream_t stream) {

@@ -136,6 +136,21 @@ def test_read_probe_validation(binding):
     assert lib.moe_hbm_read_probe(p, 4096, 0, p, None) == binding.MOE_ERR_INVALID_ARG
 
 
+def test_mfma_probe_validation(binding):
+    p = ctypes.c_void_p(ALIGNED)
+    lib = binding.lib
+    kib16 = 16 * 1024
+    assert lib.moe_mfma_probe(None, kib16, 1, 1, p, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(p, kib16, 1, 1, None, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(ctypes.c_void_p(MISALIGNED), kib16, 1, 1, p, None, None) == binding.MOE_ERR_UNSUPPORTED
+    assert lib.moe_mfma_probe(p, kib16 - 16, 1, 1, p, None, None) == binding.MOE_ERR_UNSUPPORTED
+    assert lib.moe_mfma_probe(p, kib16 + 8, 1, 1, p, None, None) == binding.MOE_ERR_UNSUPPORTED
+    assert lib.moe_mfma_probe(p, kib16, 0, 1, p, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(p, kib16, (1 << 24) + 1, 1, p, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(p, kib16, 1, 0, p, None, None) == binding.MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(p, kib16, 1, 65537, p, None, None) == binding.MOE_ERR_INVALID_ARG
+
+
 def test_rmsnorm_validation(binding):
     p = ctypes.c_void_p(ALIGNED)
     assert binding.lib.moe_rmsnorm(None, None, 0, 64, 1e-5, 0, None) == binding.MOE_OK

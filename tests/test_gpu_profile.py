@@ -69,3 +69,56 @@ def test_read_probe_reads_every_word(n_words, blocks):
     torch.cuda.synchronize()
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
     assert sink.cpu().numpy().view(np.uint32)[0] == want
+
+
+def _probe_fold_reference(ops16, blocks, iters):
+    """What the MFMA probe's sink must hold, computed on the CPU from the
+    16x16x32 bf16 MFMA's operand and result layout: lane (c, g) = (lane % 16,
+    lane // 16) supplies row c (A) or column c (B) at k = 8g .. 8g + 7, and
+    receives rows 4g .. 4g + 3 of column c of the product.  The operands are
+    small integers, so every sum is exact in fp32 and the order of the
+    hardware's additions cannot matter."""
+    n16 = ops16.size // 8
+    vec = ops16.reshape(n16, 8).astype(np.float64)
+    fold = np.uint32(0)
+    for blk in range(blocks):
+        for w in range(4):
+            lanes = np.arange(64)
+            base = ((blk * 256 + w * 64 + lanes) * 16)
+            a = np.stack([vec[(base + i) % n16] for i in range(8)])      # [8 frag][64 lane][8]
+            b = np.stack([vec[(base + 8 + i) % n16] for i in range(8)])
+            # A_i[r][k] = a[i][r + 16 (k // 8)][k % 8]; B_j[k][c] = b[j][c + 16 (k // 8)][k % 8]
+            A = np.zeros((8, 16, 32))
+            B = np.zeros((8, 32, 16))
+            for kg in range(4):
+                A[:, :, 8 * kg:8 * kg + 8] = a[:, 16 * kg:16 * kg + 16, :]
+                B[:, 8 * kg:8 * kg + 8, :] = b[:, 16 * kg:16 * kg + 16, :].transpose(0, 2, 1)
+            f = np.zeros(64, np.uint32)
+            for m in range(8):
+                for n in range(8):
+                    C = sum(A[(m + h) & 7] @ B[(n + 3 * h) & 7] for h in range(2)) * iters
+                    # lane (c, g): C[4g][c] + C[4g+1][c] + C[4g+2][c] + C[4g+3][c]
+                    s = C.reshape(4, 4, 16).sum(axis=1)  # [g][c]
+                    vals = np.array([s[l // 16][l % 16] for l in range(64)], np.float32)
+                    f ^= vals.view(np.uint32)
+            fold ^= np.bitwise_xor.reduce(f)
+    return fold
+
+
+@pytest.mark.parametrize("blocks,iters", [(1, 1), (3, 5)])
+def test_mfma_probe_products_are_exact(blocks, iters):
+    """The MFMA probe computes what the matrix-core layout says: with
+    small-integer bf16 operands (exact sums), its XOR fold equals the CPU's,
+    and its clock record is positive."""
+    from sparse_mixture_experts_select_amd import binding
+    print("\n[case] mfma probe %d workgroups x %d iterations" % (blocks, iters), flush=True)
+    g = torch.Generator().manual_seed(blocks * 100 + iters)
+    ops = torch.randint(-2, 3, (8192,), generator=g).to(torch.bfloat16)   # 16 KiB
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    binding.moe_mfma_probe(ops.cuda(), iters, blocks, sink, clocks)
+    torch.cuda.synchronize()
+    want = _probe_fold_reference(ops.float().numpy(), blocks, iters)
+    assert sink.cpu().numpy().view(np.uint32)[0] == want
+    ck = clocks.cpu().numpy().reshape(blocks, 2)
+    assert np.all(ck > 0)
