@@ -133,6 +133,33 @@ moe_status_t moe_ffn_forward_ex(const void *x, const void *w_router, const void 
                                 int64_t f, int64_t E, int64_t k, void *out, void *stream,
                                 const moe_ffn_opts_t *opts);
 
+/*
+ * For callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * moe_ffn_forward_ex with the workspace taken from a scratch array that the
+ * library holds in device memory -- a file-scope array of
+ * moe_ffn_noalloc_scratch_bytes() = 64 MiB, one copy on each GPU the library
+ * runs on, kept until the process ends.  No call allocates or frees memory:
+ * the first call on a device only looks up that device's copy of the array.
+ * Same arguments, layouts and results as moe_ffn_forward_ex (opts may be
+ * NULL: bf16, no options); opts->workspace must be NULL.  Sizes whose
+ * workspace (moe_ffn_workspace_bytes) exceeds 64 MiB return
+ * MOE_ERR_UNSUPPORTED before any launch; at d = 4096, f = 14336, E = 8,
+ * k = 2 that admits every batch up to T = 191 tokens (the streamed-weight
+ * path).  Nothing in the scratch needs to start zeroed.  Every call on one
+ * GPU uses that GPU's one array: calls that overlap on a GPU (several host
+ * threads, or streams that run concurrently) race and give undefined
+ * results; serialise them, or give each its own workspace through
+ * moe_ffn_forward_ex.
+ */
+moe_status_t moe_ffn_forward_noalloc(const void *x, const void *w_router, const void *w1,
+                                     const void *w3, const void *w2, int64_t T, int64_t d,
+                                     int64_t f, int64_t E, int64_t k, void *out, void *stream,
+                                     const moe_ffn_opts_t *opts);
+
+/* Bytes of the scratch array moe_ffn_forward_noalloc works in (64 MiB). */
+size_t moe_ffn_noalloc_scratch_bytes(void);
+
 /* Bytes of scratch one forward call needs for these sizes (0 on bad sizes). */
 size_t moe_ffn_workspace_bytes(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
                                int32_t dtype);

@@ -67,6 +67,10 @@ lib.moe_ffn_forward_f32.argtypes = _FWD_ARGS
 lib.moe_ffn_forward_f32.restype = ctypes.c_int
 lib.moe_ffn_forward_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(MoeFfnOpts)]
 lib.moe_ffn_forward_ex.restype = ctypes.c_int
+lib.moe_ffn_forward_noalloc.argtypes = _FWD_ARGS + [ctypes.POINTER(MoeFfnOpts)]
+lib.moe_ffn_forward_noalloc.restype = ctypes.c_int
+lib.moe_ffn_noalloc_scratch_bytes.argtypes = []
+lib.moe_ffn_noalloc_scratch_bytes.restype = ctypes.c_size_t
 lib.moe_ffn_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.c_int32]
 lib.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
 lib.moe_rmsnorm.argtypes = [_P, _P, _I64, _I64, ctypes.c_float, ctypes.c_int32, _P]
@@ -158,14 +162,9 @@ def moe_ffn_forward_f32(x, w_router, w1, w3, w2, k, out=None, stream=None):
     return out
 
 
-def moe_ffn_forward_ex(x, w_router, w1, w3, w2, k, out=None, stream=None, *, router_bias=None,
-                       topk_ids=None, topk_weights=None, expert_counts=None, expert_offsets=None,
-                       row_token=None, slot_row=None, h_out=None, y_out=None, residual=None,
-                       workspace=None, rmsnorm_eps=None, x_norm_out=None):
-    """The layer with options (see ``moe_ffn_opts_t``); every tensor option is
-    a GPU tensor or None.  ``rmsnorm_eps`` set: x is the residual stream h and
-    the layer runs on RMSNorm(h) (formed by the router; ``x_norm_out``, if
-    given, receives it).  Returns ``out``."""
+def _forward_with_opts(fn, x, w_router, w1, w3, w2, k, out, stream, router_bias, topk_ids,
+                       topk_weights, expert_counts, expert_offsets, row_token, slot_row, h_out,
+                       y_out, residual, workspace, rmsnorm_eps, x_norm_out):
     T, d, f, E = _shapes(x, w_router, w1, w3, w2)
     if out is None:
         out = torch.empty_like(x)
@@ -201,9 +200,40 @@ def moe_ffn_forward_ex(x, w_router, w1, w3, w2, k, out=None, stream=None, *, rou
     if rmsnorm_eps is not None:
         opts.rmsnorm_input = 1
         opts.rmsnorm_eps = float(rmsnorm_eps)
-    _check(lib.moe_ffn_forward_ex(_ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3), _ptr(w2),
-                                  T, d, f, E, k, _ptr(out), _stream(stream), ctypes.byref(opts)))
+    _check(fn(_ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3), _ptr(w2), T, d, f, E, k, _ptr(out),
+              _stream(stream), ctypes.byref(opts)))
     return out
+
+
+def moe_ffn_forward_ex(x, w_router, w1, w3, w2, k, out=None, stream=None, *, router_bias=None,
+                       topk_ids=None, topk_weights=None, expert_counts=None, expert_offsets=None,
+                       row_token=None, slot_row=None, h_out=None, y_out=None, residual=None,
+                       workspace=None, rmsnorm_eps=None, x_norm_out=None):
+    """The layer with options (see ``moe_ffn_opts_t``); every tensor option is
+    a GPU tensor or None.  ``rmsnorm_eps`` set: x is the residual stream h and
+    the layer runs on RMSNorm(h) (formed by the router; ``x_norm_out``, if
+    given, receives it).  Returns ``out``."""
+    return _forward_with_opts(lib.moe_ffn_forward_ex, x, w_router, w1, w3, w2, k, out, stream,
+                              router_bias, topk_ids, topk_weights, expert_counts, expert_offsets,
+                              row_token, slot_row, h_out, y_out, residual, workspace, rmsnorm_eps,
+                              x_norm_out)
+
+
+def moe_ffn_forward_noalloc(x, w_router, w1, w3, w2, k, out=None, stream=None, *, router_bias=None,
+                            topk_ids=None, topk_weights=None, expert_counts=None,
+                            expert_offsets=None, row_token=None, slot_row=None, h_out=None,
+                            y_out=None, residual=None, rmsnorm_eps=None, x_norm_out=None):
+    """moe_ffn_forward_ex working in the library's static scratch (no
+    allocation; see the header).  ``out`` should be given by callers that
+    cannot allocate (None allocates it here, as torch.empty_like(x))."""
+    return _forward_with_opts(lib.moe_ffn_forward_noalloc, x, w_router, w1, w3, w2, k, out, stream,
+                              router_bias, topk_ids, topk_weights, expert_counts, expert_offsets,
+                              row_token, slot_row, h_out, y_out, residual, None, rmsnorm_eps,
+                              x_norm_out)
+
+
+def moe_ffn_noalloc_scratch_bytes() -> int:
+    return int(lib.moe_ffn_noalloc_scratch_bytes())
 
 
 def moe_ffn_workspace_bytes(T, d, f, E, k, dtype=MOE_DTYPE_BF16) -> int:

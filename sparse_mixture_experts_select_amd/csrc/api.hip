@@ -203,6 +203,35 @@ moe_status_t cached_workspace(size_t need, void** out) {
     return MOE_OK;
 }
 
+// The no-allocation entry point's scratch: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (in host code it is only a stand-in): each
+// device's address is looked up once with hipGetSymbolAddress, with that
+// device current, and kept here.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+moe_status_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device index %d >= 64", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return fail(MOE_ERR_HIP, "hipGetSymbolAddress of the scratch array: %s", hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 // Stage-boundary events of profiled calls (moe_ffn_profile_begin/end).
 struct Profiler {
     bool active = false;
@@ -385,6 +414,37 @@ moe_status_t moe_ffn_forward_ex(const void* x, const void* w_router, const void*
     const int dtype = opts ? opts->dtype : MOE_DTYPE_BF16;
     return forward_impl(x, w_router, w1, w3, w2, T, d, f, E, k, out, stream, opts, dtype);
 }
+
+moe_status_t moe_ffn_forward_noalloc(const void* x, const void* w_router, const void* w1,
+                                     const void* w3, const void* w2, int64_t T, int64_t d,
+                                     int64_t f, int64_t E, int64_t k, void* out, void* stream,
+                                     const moe_ffn_opts_t* opts) {
+    const int dtype = opts ? opts->dtype : MOE_DTYPE_BF16;
+    moe_status_t st = check_sizes(T, d, f, E, k, dtype);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (opts && opts->workspace)
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_ffn_forward_noalloc uses the library's static scratch; opts->workspace must be NULL");
+    const size_t need = make_plan(T, d, f, E, k, dtype).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "these sizes need %zu bytes of scratch, above the %zu bytes the no-allocation entry "
+                    "point holds (pass a workspace to moe_ffn_forward_ex instead)",
+                    need, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != MOE_OK) return st;
+    moe_ffn_opts_t o;
+    if (opts) o = *opts;
+    else memset(&o, 0, sizeof o);
+    o.dtype = dtype;
+    o.workspace = ws;
+    o.workspace_bytes = kNoAllocScratchBytes;
+    return forward_impl(x, w_router, w1, w3, w2, T, d, f, E, k, out, stream, &o, dtype);
+}
+
+size_t moe_ffn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 size_t moe_ffn_workspace_bytes(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int32_t dtype) {
     char saved[sizeof g_err];

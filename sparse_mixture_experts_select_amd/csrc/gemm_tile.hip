@@ -668,11 +668,22 @@ hipError_t launch_tile(const void* A, const void* B0, const void* B1, void* C, f
 }  // namespace
 
 size_t tile_partials_bytes(int R, int E, int d, int f) {
-    // at most 2 cpx pieces per XCD, and at most kMaxPieces per tile
+    // Only GEMM 2 (K = f, N = d, 256-column tiles) cuts tiles.  Per XCD at
+    // most its share of the tiles, each cut into at most
+    // min(kMaxPieces, K steps / 8) pieces, and at most 2 cpx pieces in all
+    // (the schedule's limits); with fewer than 2 pieces possible nothing is
+    // cut and only the header is needed.
     const long long mtiles = (R + kBM - 1) / kBM + E;
-    const long long nt = (f + 127) / 128 > (d + 255) / 256 ? (f + 127) / 128 : (d + 255) / 256;
-    long long slots = 8 * 2 * (long long)kMaxCpx;
-    if (mtiles * nt * kMaxPieces < slots) slots = mtiles * nt * kMaxPieces;
+    const long long nt2 = (d + 255) / 256;
+    const long long per_xcd = (mtiles * nt2 + 7) / 8;
+    long long pmax = (f / kBK) / 8;
+    if (pmax > kMaxPieces) pmax = kMaxPieces;
+    long long slots = 0;
+    if (pmax >= 2) {
+        long long per = per_xcd * pmax;
+        if (per > 2 * kMaxCpx) per = 2 * kMaxCpx;
+        slots = 8 * per;
+    }
     return ((size_t)slots * kSlotFloats + kHeaderFloats) * sizeof(float);
 }
 
