@@ -110,65 +110,12 @@ __device__ __forceinline__ void stage_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-constexpr int kMaxCpx = 32;      // CUs per XCD the schedule plans for (MI355X: 32)
-constexpr int kMaxPieces = 8;      // K pieces per cut tile (GEMM 2)
-constexpr int kPieceOverhead = 16;  // per-item cost in K steps: pipeline fill, epilogue
-constexpr int kPieceTraffic = 1;    // per-piece cost in K steps: its 256 KiB partial sum
-                                    // written and read back by the fixup (measured)
 constexpr int kSlotFloats = kThreads * 256;  // one tile's fp32 accumulators
 // The partial-sum buffer starts with a header written by the tile kernel for
 // the fixup: ints [8 x] = the number of cut tiles of XCD x, then from int 64
 // one 8-int descriptor per cut tile {row0, row_end, col0, is_tail, first
 // slot, pieces}, cut tiles numbered XCD by XCD.  The slots follow.
 constexpr int kHeaderFloats = 64 + 8 * 8 * kMaxCpx;
-
-// Work of XCD x.  Workgroup IDs are dealt to the 8 XCDs round-robin, so XCD
-// x runs the workgroups with blockIdx % 8 == x; it gets the x-th run of
-// ceil(n/8) tile numbers (tiles sharing a weight panel then share one L2).  Its
-// first `full` tiles, whole rounds of its cpx CUs, run whole; the r left over
-// (fewer than cpx) are each cut into p equal K ranges when that finishes the
-// XCD's work sooner (fewer idle CUs in its last round), the pieces of one K
-// range of all r tiles running together.
-struct XcdSched {
-    int start, full, r, p;
-};
-
-__device__ __forceinline__ XcdSched xcd_schedule(int n_tiles, int x, int cpx, int KT, int max_pieces) {
-    XcdSched s;
-    const int per_xcd = (n_tiles + 7) / 8;
-    s.start = min(x * per_xcd, n_tiles);
-    const int n_x = min(s.start + per_xcd, n_tiles) - s.start;
-    s.full = (n_x / cpx) * cpx;
-    s.r = n_x - s.full;
-    s.p = 1;
-    if (s.r > 0) {
-        int best = (KT + kPieceOverhead);  // one round of whole tiles
-        for (int p = 2; p <= max_pieces; ++p) {
-            if (s.r * p > 2 * cpx || KT / p < 8) break;
-            const int cost = ((s.r * p + cpx - 1) / cpx) * ((KT + p - 1) / p + kPieceOverhead) +
-                             s.r * p * kPieceTraffic;
-            if (cost < best) {
-                best = cost;
-                s.p = p;
-            }
-        }
-    }
-    return s;
-}
-
-// First partial-sum slot and first cut-tile number of XCD x (the XCDs'
-// pieces and cut tiles are packed in XCD order).
-__device__ __forceinline__ int2 xcd_bases(int n_tiles, int x, int cpx, int KT, int max_pieces) {
-    int2 b = make_int2(0, 0);
-    for (int x2 = 0; x2 < x; ++x2) {
-        const XcdSched s = xcd_schedule(n_tiles, x2, cpx, KT, max_pieces);
-        if (s.p > 1) {
-            b.x += s.r * s.p;
-            b.y += s.r;
-        }
-    }
-    return b;
-}
 
 // ---- GEMM 1 epilogue of one tile: lane holds rows 4*lgrp + r (r = 0..3) of
 // column lrow of each fragment.  st0 and st1 are two LDS arrays of at least
@@ -294,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     // A K piece's partial-sum slot and cut-tile number, found here, where
     // they cost two wave-uniform scalars (after the K loop the search would
     // compete with the accumulators for registers).
-    int2 piece_bases = make_int2(0, 0);
+    XcdBases piece_bases{0, 0};
     if (!DUAL && piece >= 0) piece_bases = xcd_bases(n_tiles, xcd, cpx, KT, max_pieces);
 
     const int tid = threadIdx.x;
@@ -547,9 +494,9 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         rlim = row_end - row0;
         clim = N - col0;
     } else {
-        const int first_slot = piece_bases.x + rt * sc.p;
+        const int first_slot = piece_bases.slot + rt * sc.p;
         if (piece == 0 && threadIdx.x == 0) {
-            int* desc = reinterpret_cast<int*>(partials) + 64 + 8 * (piece_bases.y + rt);
+            int* desc = reinterpret_cast<int*>(partials) + 64 + 8 * (piece_bases.cut + rt);
             desc[0] = row0;
             desc[1] = row_end;
             desc[2] = col0;

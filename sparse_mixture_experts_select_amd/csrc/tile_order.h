@@ -9,9 +9,14 @@
 // row tiles x 4 column tiles, which read 8 A slabs and 4 weight slabs per K
 // step from its L2 (32 row tiles of one column tile would read 33).
 //
+// Also the schedule of a launch's tiles over the 8 XCDs (xcd_schedule): each
+// XCD's run of tile numbers, and how GEMM 2 cuts the tiles of an XCD's last,
+// partial round into K pieces.
+//
 // Plain functions of their arguments: the kernels call them on the device,
 // and the CPU tests compile this header with a host compiler to check that
-// the numbering covers every tile exactly once.
+// the numbering covers every tile exactly once and to compare the schedule
+// with the tests' own statement of it.
 #pragma once
 
 #include <cstdint>
@@ -27,6 +32,12 @@ namespace moe {
 constexpr int kBM = 256;        // rows of a full tile
 constexpr int kGroupPairs = 2;  // pairs of column tiles per group
 constexpr int kRowBlock = 8;    // row tiles per block within a group
+
+constexpr int kMaxCpx = 32;         // CUs per XCD the schedule plans for (MI355X: 32)
+constexpr int kMaxPieces = 8;       // K pieces per cut tile (GEMM 2)
+constexpr int kPieceOverhead = 16;  // per-item cost in K steps: pipeline fill, epilogue
+constexpr int kPieceTraffic = 1;    // per-piece cost in K steps: its 256 KiB partial sum
+                                    // written and read back by the fixup (measured)
 
 MOE_TILE_FN int tile_min(int a, int b) { return a < b ? a : b; }
 
@@ -90,6 +101,58 @@ MOE_TILE_FN TileGeo tile_geometry(int t, const int32_t* offsets, int E, int NT, 
         L -= per_e;
     }
     return g;
+}
+
+// Work of XCD x.  Workgroup IDs are dealt to the 8 XCDs round-robin, so XCD
+// x runs the workgroups with blockIdx % 8 == x; it gets the x-th run of
+// ceil(n/8) tile numbers (tiles sharing a weight panel then share one L2).  Its
+// first `full` tiles, whole rounds of its cpx CUs, run whole; the r left over
+// (fewer than cpx) are each cut into p equal K ranges when that finishes the
+// XCD's work sooner (fewer idle CUs in its last round), the pieces of one K
+// range of all r tiles running together.  KT: K steps of a tile.
+struct XcdSched {
+    int start, full, r, p;
+};
+
+MOE_TILE_FN XcdSched xcd_schedule(int n_tiles, int x, int cpx, int KT, int max_pieces) {
+    XcdSched s;
+    const int per_xcd = (n_tiles + 7) / 8;
+    s.start = tile_min(x * per_xcd, n_tiles);
+    const int n_x = tile_min(s.start + per_xcd, n_tiles) - s.start;
+    s.full = (n_x / cpx) * cpx;
+    s.r = n_x - s.full;
+    s.p = 1;
+    if (s.r > 0) {
+        int best = (KT + kPieceOverhead);  // one round of whole tiles
+        for (int p = 2; p <= max_pieces; ++p) {
+            if (s.r * p > 2 * cpx || KT / p < 8) break;
+            const int cost = ((s.r * p + cpx - 1) / cpx) * ((KT + p - 1) / p + kPieceOverhead) +
+                             s.r * p * kPieceTraffic;
+            if (cost < best) {
+                best = cost;
+                s.p = p;
+            }
+        }
+    }
+    return s;
+}
+
+// First partial-sum slot and first cut-tile number of XCD x (the XCDs'
+// pieces and cut tiles are packed in XCD order).
+struct XcdBases {
+    int slot, cut;
+};
+
+MOE_TILE_FN XcdBases xcd_bases(int n_tiles, int x, int cpx, int KT, int max_pieces) {
+    XcdBases b{0, 0};
+    for (int x2 = 0; x2 < x; ++x2) {
+        const XcdSched s = xcd_schedule(n_tiles, x2, cpx, KT, max_pieces);
+        if (s.p > 1) {
+            b.slot += s.r * s.p;
+            b.cut += s.r;
+        }
+    }
+    return b;
 }
 
 }  // namespace moe

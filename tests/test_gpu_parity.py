@@ -98,6 +98,32 @@ def test_small_shapes(T, d, f, E, k, dtype):
                        r["gpu"]["out"].view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
 
 
+CUT_CASES = [
+    # T, d, f, E, k, piece counts GEMM 2's schedule cuts tiles into (E = 1 or
+    # k = E: every expert's row count is known, so the tile plan is)
+    (256, 2048, 2048, 1, 1, {8}),
+    (256, 2048, 1536, 1, 1, {6}),
+    (256, 2048, 1280, 1, 1, {5}),
+    (512, 1024, 2048, 2, 2, {5}),       # two cut tiles on every XCD
+    (768, 1536, 2048, 2, 2, {8, 4}),    # one cut tile on some XCDs, five on others
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,k,pieces", CUT_CASES)
+def test_gemm2_tiles_cut_into_k_pieces(T, d, f, E, k, pieces):
+    """GEMM 2's last round cut into 5, 6 or 8 K pieces (the counts the
+    full-size workloads use), the fixup summing them: every row of out, h
+    and y against the oracle."""
+    import tile_plan
+    cpx = torch.cuda.get_device_properties(0).multi_processor_count // 8
+    assert tile_plan.gemm2_pieces([T * k // E] * E, d, f, cpx) == pieces
+    banner("GEMM 2 cut into %s K pieces: T=%d d=%d f=%d E=%d k=%d" % (sorted(pieces), T, d, f, E, k))
+    inp = case(T, d, f, E, torch.bfloat16, seed=T + d + f, label="cut")
+    r = PT.full_check(inp, k)
+    np.testing.assert_array_equal(PT.to_np(r["gpu"]["counts"]), [T * k // E] * E)
+    print("near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
+
+
 def test_batch_with_h_past_2gib():
     """h = 65600 x 16384 bf16 is past 2 GiB: the GEMMs fall back from the
     256-row tile kernels (32-bit buffer offsets) to the 128-row grouped ones."""
