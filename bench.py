@@ -45,20 +45,27 @@ GEMM1_KERNEL = {
     "decode": ("gemm_stream.hip", r"stream_gemm_kernel(<true, false|ILb1ELb0E)"),
     "prefill": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
     "skewed": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
+    "stack": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
 }
 CALIBRATION_BYTES = 1 << 30
 # Profiling commands behind the committed summaries; {out} is the rocprofv3
 # output directory that the summarizer is then pointed at.
-PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d {out} -o run -- "
+PMC_COMMAND = ("timeout -s KILL 150 rocprofv3 --pmc {counter} --output-format csv -d {out} -o run -- "
                "python3 bench.py --steps 3 --warmup 1 --stack off --skewed off --sweep off "
                "--no-cpu-baseline --calibrate-copy")
 # The skewed workload runs the same w1/w3 kernel as prefill, so its counters
 # come from a run of their own.
-SKEWED_PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counter} --output-format csv -d {out} "
+SKEWED_PMC_COMMAND = ("timeout -s KILL 150 rocprofv3 --pmc {counter} --output-format csv -d {out} "
                       "-o run -- python3 bench.py --workload skewed --secondary none --steps 3 "
                       "--warmup 1 --stack off --sweep off --no-cpu-baseline --calibrate-copy")
+# The 32-block stack (T = 2048) runs the same w1/w3 kernel as prefill; in a
+# run of the stack beside the decode workload (whose w1/w3 kernel is the
+# streamed one) every dispatch of the tile kernel is a stack layer.
+STACK_PMC_COMMAND = ("timeout -s KILL 300 rocprofv3 --pmc {counter} --output-format csv -d {out} "
+                     "-o run -- python3 bench.py --secondary none --skewed off --sweep off "
+                     "--steps 3 --warmup 1 --stack on --no-cpu-baseline --calibrate-copy")
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE GRBM_COUNT"
-MFMA_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv "
+MFMA_COMMAND = ("timeout -s KILL 150 rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv "
                 "-d {out} -o run -- python3 bench.py --workload prefill --secondary none "
                 "--steps 3 --warmup 1 --stack off --skewed off --sweep off --no-cpu-baseline")
 SIMDS = 256 * 4          # MI355X: 256 CUs x 4 SIMDs
@@ -307,7 +314,7 @@ def run_stack(steps, warmup, binding, inputs, torch):
                      "achieved": round(g_flops / (g_ms * 1e-3) / 1e12, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "avg_launch_ms": round(g_ms, 5), "traffic": None},
+                     "avg_launch_ms": round(g_ms, 5), "traffic": committed_traffic("stack")},
         "layer": {"tflops_active": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
                   "mfma_frac": round(flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                   "hbm_gbs": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -593,13 +600,16 @@ def _counter_rows(run_dir):
         return list(csv.DictReader(fh))
 
 
-def summarize_counters(fetch_dir, write_dir, skewed=False):
+def summarize_counters(fetch_dir, write_dir, which="default"):
     """Turn two rocprofv3 --pmc runs of PMC_COMMAND (FETCH_SIZE, then
     WRITE_SIZE) into profiles/gemm1_swiglu_<workload>_traffic.txt for the
-    decode and prefill workloads, or two runs of SKEWED_PMC_COMMAND into the
-    skewed workload's: HBM bytes per launch of the w1/w3 kernel, each counter
-    scaled by what it reads for the 1 GiB calibration copies run in the same
+    decode and prefill workloads, or two runs of SKEWED_PMC_COMMAND
+    (which="skewed") or STACK_PMC_COMMAND (which="stack") into that
+    workload's: HBM bytes per launch of the w1/w3 kernel, each counter scaled
+    by what it reads for the 1 GiB calibration copies run in the same
     process."""
+    skewed = which == "skewed"
+    stack = which == "stack"
     import re
     import statistics
 
@@ -621,7 +631,9 @@ def summarize_counters(fetch_dir, write_dir, skewed=False):
                     if r["Counter_Name"] == name and re.search(pattern, r["Kernel_Name"])]
             if vals:
                 per[name] = vals
-        if len(per) != 2 or (wl == "skewed") != skewed:
+        if len(per) != 2 or (wl == "skewed") != skewed or (wl == "stack") != stack:
+            continue
+        if which == "default" and wl not in ("decode", "prefill"):
             continue
         fetch_kib = statistics.mean(per["FETCH_SIZE"])
         write_kib = statistics.mean(per["WRITE_SIZE"])
@@ -630,11 +642,12 @@ def summarize_counters(fetch_dir, write_dir, skewed=False):
         with open(out, "w") as fh:
             fh.write("# HBM traffic of the w1/w3 grouped GEMM + SwiGLU kernel, %s workload\n" % wl)
             fh.write("# kernel: %s (source %s)\n" % (pattern, src))
-            cmd = SKEWED_PMC_COMMAND if skewed else PMC_COMMAND
+            cmd = SKEWED_PMC_COMMAND if skewed else (STACK_PMC_COMMAND if stack else PMC_COMMAND)
             for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
                 fh.write("# command (%s): %s\n" % (name, cmd.format(counter=name, out=d)))
             fh.write("# summarized by: python3 bench.py --summarize-counters %s %s%s\n"
-                     % (fetch_dir, write_dir, " --counters-skewed" if skewed else ""))
+                     % (fetch_dir, write_dir,
+                        "" if which == "default" else " --counters-workload " + which))
             fh.write("# calibration: %d-byte device copy reads FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f "
                      "KiB\n" % (CALIBRATION_BYTES, calib["FETCH_SIZE"], calib["WRITE_SIZE"]))
             fh.write("fetch_scale = %.4f\n" % factor["FETCH_SIZE"])
@@ -753,9 +766,8 @@ def summarize_trace(trace_dir):
     phase = None  # the router launch that opened the current layer call
     garbled = False
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-    for r in rows:
-        if "moe" not in r["Kernel_Name"] and "copyBuffer" not in r["Kernel_Name"]:
-            continue
+    rows = [r for r in rows if "moe" in r["Kernel_Name"] or "copyBuffer" in r["Kernel_Name"]]
+    for i, r in enumerate(rows):
         name = _short_kernel_name(r["Kernel_Name"])
         if "_Accum" in name:
             # rocprofv3 prints combine_kernel<bf16, true> (the K-slice form,
@@ -763,8 +775,12 @@ def summarize_trace(trace_dir):
             # benchmark runs) with this garbled template list
             name, garbled = "combine_kernel<bf16, true>", True
         grid = int(r["Grid_Size_X"])
-        if name.startswith("router_topk_kernel"):
-            phase = (name, grid)
+        if name.startswith("router_"):
+            # a router launch opens a layer call; the launch after it (the
+            # grouping, sized by T*k) tells workloads apart whose routers
+            # share a grid
+            nxt = rows[i + 1] if i + 1 < len(rows) else r
+            phase = (name, grid, nxt["Kernel_Name"], int(nxt["Grid_Size_X"]))
         key = (phase, name, grid)
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         g = groups.setdefault(key, {"d": [], "first": int(r["Dispatch_Id"]), "row": r})
@@ -782,13 +798,15 @@ def summarize_trace(trace_dir):
         if garbled:
             fh.write("# combine_kernel<bf16, true>: rocprofv3 printed this instantiation's name as "
                      "'combine_kernel<bool _Accum, bool, E>'\n")
-        fh.write("%-44s %9s %6s %10s %10s %10s %5s %5s %6s\n" % (
-            "kernel", "grid", "calls", "avg_us", "min_us", "max_us", "vgpr", "agpr", "lds"))
+        fh.write("%-44s %9s %6s %10s %10s %10s %5s %5s %6s %7s\n" % (
+            "kernel", "grid", "calls", "avg_us", "min_us", "max_us", "vgpr", "agpr", "lds",
+            "scratch"))
         for (_, name, grid), g in sorted(groups.items(), key=lambda kv: kv[1]["first"]):
             r = g["row"]
-            fh.write("%-44s %9d %6d %10.2f %10.2f %10.2f %5s %5s %6s\n" % (
+            fh.write("%-44s %9d %6d %10.2f %10.2f %10.2f %5s %5s %6s %7s\n" % (
                 name[:44], grid, len(g["d"]), statistics.mean(g["d"]), min(g["d"]), max(g["d"]),
-                r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"]))
+                r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"],
+                r.get("Scratch_Size", "?")))
     log("[bench] wrote", out)
 
 
@@ -814,14 +832,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--counters-skewed", action="store_true",
-                    help="with --summarize-counters: the runs are of SKEWED_PMC_COMMAND")
+    ap.add_argument("--counters-workload", default="default", choices=["default", "skewed", "stack"],
+                    help="with --summarize-counters: the runs are of PMC_COMMAND (default), "
+                         "SKEWED_PMC_COMMAND or STACK_PMC_COMMAND")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     args = ap.parse_args()
 
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, skewed=args.counters_skewed)
+        summarize_counters(*args.summarize_counters, which=args.counters_workload)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)

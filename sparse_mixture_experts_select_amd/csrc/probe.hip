@@ -45,12 +45,16 @@ __global__ __launch_bounds__(256, 1) void mfma_probe_kernel(const uint4* __restr
                                                             int iters, uint32_t* __restrict__ sink,
                                                             unsigned long long* __restrict__ clocks) {
     __shared__ uint32_t hold[kProbeHold];
-    const size_t base = ((size_t)blockIdx.x * 256 + threadIdx.x) * 16;
+    // 16 consecutive 16-byte vectors per thread, wrapping at the end of ops
+    // (n16 >= 1024)
+    const size_t base = ((size_t)blockIdx.x * 256 + threadIdx.x) * 16 % n16;
     bf16x8 a[8], b[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        a[i] = __builtin_bit_cast(bf16x8, ops[(base + i) % n16]);
-        b[i] = __builtin_bit_cast(bf16x8, ops[(base + 8 + i) % n16]);
+    for (int i = 0; i < 16; ++i) {
+        const size_t j = base + i < n16 ? base + i : base + i - n16;
+        const bf16x8 v = __builtin_bit_cast(bf16x8, ops[j]);
+        if (i < 8) a[i] = v;
+        else b[i - 8] = v;
     }
     floatx4 acc[8][8];
 #pragma unroll
@@ -79,15 +83,19 @@ __global__ __launch_bounds__(256, 1) void mfma_probe_kernel(const uint4* __restr
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     const unsigned long long c1 = __builtin_amdgcn_s_memtime();
     const unsigned long long t1 = __builtin_amdgcn_s_memrealtime();
-    uint32_t f = hold[threadIdx.x];  // 0: only keeps the LDS reservation
+    // (thread index formed afresh, so nothing lane-dependent is kept across
+    // the loop beside the accumulators and operands)
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int tid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 64 + lane;
+    uint32_t f = hold[tid];  // 0: only keeps the LDS reservation
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int n = 0; n < 8; ++n)
             f ^= __float_as_uint(acc[m][n][0] + acc[m][n][1] + acc[m][n][2] + acc[m][n][3]);
     for (int off = 32; off >= 1; off >>= 1) f ^= __shfl_xor(f, off, 64);
-    if ((threadIdx.x & 63) == 0) atomicXor(sink, f);
-    if (clocks != nullptr && threadIdx.x == 0) {
+    if (lane == 0) atomicXor(sink, f);
+    if (clocks != nullptr && tid == 0) {
         clocks[2 * blockIdx.x] = c1 - c0;
         clocks[2 * blockIdx.x + 1] = t1 - t0;
     }
