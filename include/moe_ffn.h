@@ -162,7 +162,7 @@ size_t moe_ffn_noalloc_scratch_bytes(void);
 
 /* Bytes of scratch one forward call needs for these sizes (0 on bad sizes). */
 size_t moe_ffn_workspace_bytes(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k,
-                               int32_t dtype);
+                               moe_dtype_t dtype);
 
 /*
  * Unit-gain RMSNorm of each row, x[t,i] = h[t,i] / sqrt(mean_i h[t,i]^2 + eps),
@@ -173,7 +173,7 @@ size_t moe_ffn_workspace_bytes(int64_t T, int64_t d, int64_t f, int64_t E, int64
  * of 4 for fp32; eps >= 0).
  */
 moe_status_t moe_rmsnorm(const void *h, void *x, int64_t T, int64_t d, float eps,
-                         int32_t dtype, void *stream);
+                         moe_dtype_t dtype, void *stream);
 
 /*
  * Per-stage timing with HIP events, for benchmarks and tools.  Between

@@ -446,7 +446,7 @@ moe_status_t moe_ffn_forward_noalloc(const void* x, const void* w_router, const 
 
 size_t moe_ffn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
-size_t moe_ffn_workspace_bytes(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int32_t dtype) {
+size_t moe_ffn_workspace_bytes(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, moe_dtype_t dtype) {
     char saved[sizeof g_err];
     memcpy(saved, g_err, sizeof g_err);
     const moe_status_t st = check_sizes(T, d, f, E, k, dtype);
@@ -455,7 +455,7 @@ size_t moe_ffn_workspace_bytes(int64_t T, int64_t d, int64_t f, int64_t E, int64
     return make_plan(T, d, f, E, k, dtype).total;
 }
 
-moe_status_t moe_rmsnorm(const void* h, void* x, int64_t T, int64_t d, float eps, int32_t dtype,
+moe_status_t moe_rmsnorm(const void* h, void* x, int64_t T, int64_t d, float eps, moe_dtype_t dtype,
                          void* stream) {
     if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32)
         return fail(MOE_ERR_INVALID_ARG, "dtype %d is neither MOE_DTYPE_BF16 nor MOE_DTYPE_F32", dtype);

@@ -75,7 +75,9 @@ def brute_force_layer(case, k, bias=None):
     if bias is not None:
         logits = logits + np.asarray(bias, np.float64)[None, :]
     T, E = logits.shape
-    order = np.argsort(-logits.astype(np.float32), axis=1, kind="stable")[:, :k]
+    # selection on the double-precision logits themselves (stable: the lower
+    # index first on exact ties), independent of the oracle's binary32 reading
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
     masked = np.full_like(logits, -np.inf)
     rows = np.arange(T)[:, None]
     masked[rows, order] = logits[rows, order]
@@ -133,12 +135,37 @@ def check_brute_force(seed=3, dtype="f32"):
     """Oracle = brute force over every expert with masked top-k (tiny sizes)."""
     for (T, d, f, E, k) in [(33, 24, 40, 8, 2), (17, 16, 24, 6, 3), (9, 8, 8, 4, 1)]:
         c = random_case(T, d, f, E, seed + E, dtype)
-        ref, order, weights, _ = brute_force_layer(c, k)
+        ref, order, weights, logits = brute_force_layer(c, k)
         r = oracle.moe_tokens(c["x"], c["w_router"], c["w1"], c["w3"], c["w2"], k)
-        np.testing.assert_array_equal(r["ids"], order)
-        assert np.allclose(r["gates"], weights[np.arange(T)[:, None], order], atol=1e-13, rtol=0)
+        # the oracle selects on binary32-rounded logits (the GPU's precision);
+        # that can only differ from a double-precision selection where two
+        # logits of the order lie within binary32 rounding of each other
+        srt = -np.sort(-logits, axis=1)
+        gaps = np.abs(np.diff(srt[:, :min(k + 1, E)], axis=1))
+        resolved = np.all(gaps > 2.0 ** -23 * np.abs(srt[:, :1]) * 2, axis=1)
+        assert resolved.sum() >= T - 1, "random logits should almost never tie in binary32"
+        np.testing.assert_array_equal(r["ids"][resolved], order[resolved])
+        g_ref = weights[np.arange(T)[:, None], order]
+        assert np.allclose(r["gates"][resolved], g_ref[resolved], atol=1e-13, rtol=0)
         scale = np.abs(ref).max()
-        assert np.abs(r["out"] - ref).max() <= 1e-11 * scale
+        assert np.abs(r["out"][resolved] - ref[resolved]).max() <= 1e-11 * scale
+
+
+def check_binary32_tie_reading():
+    """Reading R3: two logits that differ in double precision but round to
+    the same binary32 value count as tied, and the tie goes to the lower
+    expert index.  One token, x = [1, 1], so the logits are the column sums
+    of the router matrix: expert 1's logit exceeds expert 0's by 2^-30 (exact
+    in double, below binary32 resolution at 1), expert 2 trails both."""
+    x = np.ones((1, 2), np.float32)
+    wr = np.array([[1.0, 1.0, 0.5], [0.0, 2.0 ** -30, 0.0]], np.float32)
+    logits, ids, gates = oracle.route(x, wr, 1)
+    assert logits[0, 1] - logits[0, 0] == 2.0 ** -30
+    assert ids[0, 0] == 0          # the binary32 tie goes to the lower index
+    logits, ids, gates = oracle.route(x, wr, 2)
+    assert list(ids[0]) == [0, 1]
+    # the softmax itself uses the double-precision logits
+    assert abs(gates[0, 1] - scipy.special.expit(2.0 ** -30)) <= 1e-15
 
 
 def check_identical_experts(seed=4):
@@ -334,7 +361,8 @@ def check_parameter_counts():
 
 
 ALL_FAST_PINS = [
-    check_gate_invariants, check_k_distinct, check_brute_force, check_identical_experts,
+    check_gate_invariants, check_k_distinct, check_brute_force, check_binary32_tie_reading,
+    check_identical_experts,
     check_special_k, check_all_ties, check_bias, check_invariances, check_silu,
     check_forced, check_rmsnorm, check_skewed_routing,
 ]

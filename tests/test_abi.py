@@ -178,3 +178,13 @@ def test_profile_validation(binding):
     assert binding.lib.moe_ffn_profile_begin(1000001, 0) == binding.MOE_ERR_INVALID_ARG
     assert binding.moe_ffn_stage_name(3) == "gemm1_swiglu"
     assert binding.moe_ffn_stage_name(binding.MOE_NUM_STAGES) == ""
+
+
+def test_unknown_dtype_codes_are_refused(binding):
+    """moe_rmsnorm and moe_ffn_workspace_bytes take a moe_dtype_t: a code that
+    names no dtype is refused (0 bytes, MOE_ERR_INVALID_ARG)."""
+    lib = binding.lib
+    assert lib.moe_ffn_workspace_bytes(8, 128, 128, 8, 2, 7) == 0
+    assert lib.moe_ffn_workspace_bytes(8, 128, 128, 8, 2, binding.MOE_DTYPE_BF16) > 0
+    p = ctypes.c_void_p(ALIGNED)
+    assert lib.moe_rmsnorm(p, p, 4, 128, ctypes.c_float(1e-5), 7, None) == binding.MOE_ERR_INVALID_ARG
