@@ -515,8 +515,9 @@ def device_facts(torch):
 
 def read_probe(torch, binding, nbytes=4 << 30, reps=3):
     """Measured streaming-read rate of this GPU: the library's read probe
-    (16-byte loads in a grid-stride loop) over a buffer far larger than the
-    256 MiB MALL, best over a few grid sizes and `reps` timed passes each."""
+    (nontemporal 16-byte loads, eight in flight, in a grid-stride loop) over
+    a buffer far larger than the 256 MiB MALL, best over a few grid sizes and
+    `reps` timed passes each."""
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     best = None
@@ -950,7 +951,7 @@ def main():
     if bound == "hbm":
         probe, blocks = read_probe(torch, binding)
         rec["read_probe"] = {
-            "what": "streaming read of a 4 GiB buffer, 16-byte loads, %d workgroups of 256 "
+            "what": "streaming read of a 4 GiB buffer, nontemporal 16-byte loads, %d workgroups of 256 "
                     "(moe_hbm_read_probe)" % blocks,
             "gbs": round(probe, 1),
             "gemm1_frac_of_probe": round(rec["roofline"]["achieved"] / probe, 4),

@@ -199,10 +199,10 @@ moe_status_t moe_ffn_profile_end(float *stage_ms, int32_t *calls);
 const char *moe_ffn_stage_name(int32_t stage);
 
 /*
- * Measurement aid, not part of the layer: a plain streaming read of `bytes`
- * bytes of device memory at buf (16-byte aligned, bytes a multiple of 16) by
+ * Measurement aid, not part of the layer: a streaming read of `bytes` bytes
+ * of device memory at buf (16-byte aligned, bytes a multiple of 16) by
  * `blocks` workgroups of 256 threads (1..65536), each reading 16-byte vectors
- * in a grid-stride loop.  *sink (a device uint32) receives an XOR fold of the
+ * marked nontemporal in a grid-stride loop.  *sink (a device uint32) receives an XOR fold of the
  * data, which only keeps the loads live.  Timing it over a buffer far larger
  * than the 256 MiB MALL gives the read rate a streaming kernel can reach on
  * this GPU, the measured ceiling beside the 8 TB/s datasheet figure.

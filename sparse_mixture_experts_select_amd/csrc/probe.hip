@@ -1,11 +1,12 @@
 // probe.hip -- measurement aids, not part of the layer:
 //
-// read_probe_kernel: a plain streaming read of a device buffer, the measured
+// read_probe_kernel: a streaming read of a device buffer, the measured
 // ceiling that the weight-streaming (HBM-bound) kernels are compared with
 // beside the 8 TB/s datasheet figure.  Each thread reads 16-byte vectors in a
-// grid-stride loop, four in flight per iteration, and folds them with XOR so
-// no load is dead; one atomic per wave writes the fold to `sink` (its value
-// has no meaning).
+// grid-stride loop, eight in flight per iteration, marked nontemporal (as the
+// streamed GEMMs' weight loads are: HBM serves such a stream at ~7.2 TB/s,
+// plain loads at ~6.4), and folds them with XOR so no load is dead; one
+// atomic per wave writes the fold to `sink` (its value has no meaning).
 //
 // mfma_probe_kernel: bf16 matrix-core work with no memory traffic, the
 // measured ceiling that the MFMA-bound tile GEMMs are compared with beside
@@ -23,18 +24,22 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ uint32_t fold(const uint4& v) { return v.x ^ v.y ^ v.z ^ v.w; }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t fold(const u32x4& v) { return v[0] ^ v[1] ^ v[2] ^ v[3]; }
 
-__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16,
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4* __restrict__ p, size_t n16,
                                                          uint32_t* __restrict__ sink) {
     const size_t stride = (size_t)gridDim.x * 256;
     size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     uint32_t acc = 0;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-        acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= fold(v[u]);
     }
-    for (; i < n16; i += stride) acc ^= fold(p[i]);
+    for (; i < n16; i += stride) acc ^= fold(__builtin_nontemporal_load(p + i));
     for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
     if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
 }
@@ -113,7 +118,7 @@ hipError_t launch_mfma_probe(const void* ops, size_t bytes, int iters, int block
 hipError_t launch_read_probe(const void* buf, size_t bytes, int blocks, uint32_t* sink,
                              hipStream_t stream) {
     hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4*>(buf), bytes / 16, sink);
+                       reinterpret_cast<const u32x4*>(buf), bytes / 16, sink);
     return hipGetLastError();
 }
 
