@@ -51,7 +51,6 @@ struct Plan {
     int variant = GEMM_LARGE_M;
     int splits = 1;
     bool g1_ksplit = false;  // streamed GEMM 1: split K over the waves of a workgroup
-    int mf = 1;              // streamed GEMMs: 16-row fragments per tile
     size_t ids = 0, gates = 0, counts = 0, offsets = 0, slot_row = 0, row_token = 0, scan = 0;
     size_t x_perm = 0, h = 0, y = 0, partials = 0, total = 0;
 };
@@ -66,33 +65,32 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
         const bool tile_ok = R * (d > f ? d : f) * 2 < ((int64_t)1 << 31) &&
                              d * f * 2 < ((int64_t)1 << 31);
         if (R < 48 * E) {
-            // Under ~48 rows per expert: stream the weights, with tiles of 1,
-            // 2 or 4 row fragments of 16.
+            // Under ~48 rows per expert: stream the weights, in row tiles of
+            // up to 64 rows (1, 2 or 4 fragments of 16, chosen per tile on the
+            // device from the expert's row count).
             p.variant = GEMM_STREAM;
-            p.mf = R <= 12 * E ? 1 : (R <= 24 * E ? 2 : 4);
-            int64_t mt = (R + 16 * p.mf - 1) / (16 * p.mf);
-            if (mt < busy_experts) mt = busy_experts;
             // GEMM 1 gives each wave a 128-column slab over all of K; when
             // that leaves most CUs idle (one or two tokens), split K over the
-            // waves of a workgroup instead.
-            p.g1_ksplit = p.mf == 1 && mt * ((f + 511) / 512) < 128;
+            // waves of a workgroup instead (16-row tiles).
+            int64_t mt16 = (R + 15) / 16;
+            if (mt16 < busy_experts) mt16 = busy_experts;
+            p.g1_ksplit = R <= 12 * E && mt16 * ((f + 511) / 512) < 128;
             // GEMM 2 gives each wave a 128-column slab, the 4 waves of a
             // workgroup 4 adjacent slabs (512 contiguous columns of every w2
             // row, as GEMM 1 reads w1 and w3), and cuts K across workgroups;
             // the combine adds the K-slice partials.  The cut is sized for
-            // about 208 streaming workgroups (256 with 4 row fragments per
-            // tile), counting the experts expected to hold rows when R
-            // assignments spread evenly over E (the routing itself is not
-            // known on the host; workgroups of empty experts exit at once).
-            // Measured at Mixtral shapes for T = 1..128: 170-230 active
-            // workgroups streamed fastest (decode GEMM 2: 154 us with 3
-            // slices, 161 with 4).
+            // about 208 streaming workgroups (256 above 12 rows per expert),
+            // counting the experts expected to hold rows when R assignments
+            // spread evenly over E (the routing itself is not known on the
+            // host; workgroups of empty experts exit at once).  Measured at
+            // Mixtral shapes: 3 slices at 8 rows per expert (decode), 4 at
+            // 16-40 rows per expert streamed fastest.
             const double e_act = std::max(std::min((double)k, (double)E),
                                           E * (1.0 - std::pow(1.0 - 1.0 / E, (double)R)));
             const double rows_per = (double)R / e_act;
-            const double mt_act = std::max(1.0, std::ceil(rows_per / (16.0 * p.mf)));
+            const double mt_act = std::max(1.0, std::ceil(rows_per / 64.0));
             const double tiles2 = (double)((d + 511) / 512) * e_act * mt_act;
-            int64_t s = std::lround((p.mf >= 4 ? 256.0 : 208.0) / tiles2);
+            int64_t s = std::lround((rows_per > 12.0 ? 256.0 : 208.0) / tiles2);
             int64_t smax = f / 128;
             if (smax > 16) smax = 16;
             if (smax < 1) smax = 1;
@@ -360,11 +358,11 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     else skip(2);
     mark(3);
     if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM) {
-        LAUNCH(launch_gemm1_swiglu_stream(x, row_token, w1, w3, offsets, R, Ei, di, fi, plan.mf,
+        LAUNCH(launch_gemm1_swiglu_stream(x, row_token, w1, w3, offsets, R, Ei, di, fi,
                                           plan.g1_ksplit, h, stream),
                "gemm1_swiglu");
         mark(4);
-        LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.mf, plan.splits, y, stream), "gemm2");
+        LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");
     } else if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_TILE256) {
         float* partials = reinterpret_cast<float*>(ws + plan.partials);
         LAUNCH(launch_gemm1_swiglu_tile(x_perm, w1, w3, offsets, R, Ei, di, fi, kb, partials, h, stream),

@@ -65,14 +65,14 @@ hipError_t launch_gemm2_f32(const void* h, const void* w2, const int32_t* offset
                             int f, int d, float* y, hipStream_t stream);
 
 // The same two contractions for batches with few rows per expert: weights are
-// streamed from HBM into registers (16-row tiles, 128-column slabs).
+// streamed from HBM into registers (row tiles of up to 64 rows, in 16-row
+// fragments sized per tile on the device; 128-column slabs).
 // (reads the token rows of x through row_token: no gathered copy is needed)
 hipError_t launch_gemm1_swiglu_stream(const void* x, const int32_t* row_token, const void* w1,
                                       const void* w3, const int32_t* offsets, int R, int E, int d,
-                                      int f, int mf, bool ksplit_waves, void* h,
-                                      hipStream_t stream);
+                                      int f, bool ksplit_waves, void* h, hipStream_t stream);
 hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* offsets, int R, int E,
-                               int f, int d, int mf, int splits, float* y, hipStream_t stream);
+                               int f, int d, int splits, float* y, hipStream_t stream);
 
 // The same two contractions for batches with many rows per expert: 256x256
 // macro tiles staged through LDS.  In GEMM 2 each XCD's last, partial round

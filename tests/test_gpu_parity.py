@@ -160,12 +160,18 @@ def test_imbalanced_and_empty_experts():
     assert counts[3] == 300 and counts[5:].sum() == 0
 
 
-def test_streamed_path_with_one_heavy_expert():
-    banner("streamed path, expert 2 takes all 40 tokens (3 row tiles)")
+@pytest.mark.parametrize("T", [40, 70, 100, 150])
+def test_streamed_path_with_one_heavy_expert(T):
+    # expert 2 takes every token (one of each token's two picks), so its
+    # row tiles are: T = 40: one tile of 40 rows (4 fragments, the last
+    # partial); 70: 64 + 6 rows (4 fragments, then 1); 100: 64 + 36 (4 and a
+    # partial 4); 150: 64 + 64 + 22 (4, 4, then 2).  The other experts share
+    # the second picks: one-fragment tiles, and two-fragment ones at T = 150.
+    banner("streamed path, expert 2 takes all %d tokens" % T)
     bias = [0.0, 0.0, 40.0, 0.0, 0.0, 0.0, 0.0, 0.0]
-    inp = case(40, 128, 256, 8, torch.bfloat16, seed=11, bias=bias, label="heavy")
+    inp = case(T, 128, 256, 8, torch.bfloat16, seed=11 + T, bias=bias, label="heavy")
     r = PT.full_check(inp, 2)
-    assert PT.to_np(r["gpu"]["counts"])[2] == 40
+    assert PT.to_np(r["gpu"]["counts"])[2] == T
 
 
 def test_zero_tokens_leaves_out_untouched():
