@@ -53,13 +53,14 @@
 // The DMA lane order fixes the LDS address, so each lane simply loads the
 // global chunk that belongs at its swizzled LDS position.
 //
-// Order.  Tiles are numbered by expert, then groups of two pairs of column
-// tiles (four column tiles); within a group, the full-row tiles in blocks of
-// 8 row tiles (rows fastest, then the group's columns), then the group's
-// tail tiles, one per pair.  Each XCD takes a contiguous run of ceil(n/8)
-// tile numbers (workgroup IDs are dealt to the 8 XCDs round-robin), so the
-// workgroups that run together on an XCD share A rows and weight panels in
-// one L2: an expert with many rows runs as 8 x 4 blocks of tiles.
+// Order.  Tiles are numbered by expert, then bands of 8 full row tiles (the
+// last band of an expert also takes its tail row); within a band, pairs of
+// column tiles in order, each pair's full-row tiles rows fastest, then its
+// tail tile.  Each XCD takes a contiguous run of ceil(n/8) tile numbers
+// (workgroup IDs are dealt to the 8 XCDs round-robin), so the workgroups
+// that run together on an XCD share A rows and weight panels in one L2: an
+// expert with many rows runs as rounds of 8 row tiles x 4 column tiles, and
+// consecutive rounds of a band keep its 8 A slabs.
 //
 // Last round (GEMM 2).  An XCD's tiles run in rounds of its CUs; the tiles
 // of its last, partial round may be cut into p equal K ranges (p chosen per

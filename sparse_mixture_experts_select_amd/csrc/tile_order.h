@@ -2,12 +2,15 @@
 // (gemm_tile.hip): which expert, rows and column tile tile number t covers,
 // from the per-expert row offsets alone.
 //
-// Tiles are numbered by expert, then groups of kGroupPairs pairs of column
-// tiles; within a group, the full-row tiles in blocks of kRowBlock row tiles
-// (rows fastest, then the group's columns), then the group's tail tiles, one
-// per pair.  An XCD's round of 32 tiles on an expert with many rows is then 8
-// row tiles x 4 column tiles, which read 8 A slabs and 4 weight slabs per K
-// step from its L2 (32 row tiles of one column tile would read 33).
+// Tiles are numbered by expert, then bands of kRowBlock full row tiles (the
+// last band of an expert takes its remaining full rows and its tail row);
+// within a band, pairs of column tiles in order, and within a pair the
+// band's full-row tiles, rows fastest, column by column, then the pair's
+// tail tile.  An XCD's round of 32 tiles on an expert with many rows is then
+// 8 row tiles x 4 column tiles, and a round that straddles two groups of
+// columns still reads the same 8 A slabs (8 slabs + 5 weight panels per K
+// step from its L2; an order in blocks of 8 rows x 4 columns, rows first,
+// makes straddling rounds read 16 slabs + 4 panels).
 //
 // Also the schedule of a launch's tiles over the 8 XCDs (xcd_schedule): each
 // XCD's run of tile numbers, and how GEMM 2 cuts the tiles of an XCD's last,
@@ -29,9 +32,8 @@
 
 namespace moe {
 
-constexpr int kBM = 256;        // rows of a full tile
-constexpr int kGroupPairs = 2;  // pairs of column tiles per group
-constexpr int kRowBlock = 8;    // row tiles per block within a group
+constexpr int kBM = 256;      // rows of a full tile
+constexpr int kRowBlock = 8;  // full row tiles per band
 
 constexpr int kMaxCpx = 32;         // CUs per XCD the schedule plans for (MI355X: 32)
 constexpr int kMaxPieces = 8;       // K pieces per cut tile (GEMM 2)
@@ -74,25 +76,41 @@ MOE_TILE_FN TileGeo tile_geometry(int t, const int32_t* offsets, int E, int NT, 
         const int tail = (rem > 0 && rem <= 128) ? 1 : 0;
         const int per_e = mt_n * NT + tail * NTP;
         if (L < per_e) {
-            // group q of up to kGroupPairs pairs of column tiles (the last
-            // group may hold fewer, and its last pair one column tile when NT
-            // is odd): its full-row tiles in blocks of kRowBlock row tiles,
-            // rows fastest, then the group's tail tiles, one per pair
-            const int full_group = mt_n * 2 * kGroupPairs + tail * kGroupPairs;
-            const int q = tile_min(L / full_group, (NTP - 1) / kGroupPairs);
-            const int r = L - q * full_group;
-            const int c_first = 2 * kGroupPairs * q;                     // first column tile
-            const int n_cols = tile_min(2 * kGroupPairs, NT - c_first);  // column tiles in the group
+            // n_band bands of kRowBlock rows, then the last band: the
+            // remaining full rows (a whole kRowBlock when they divide evenly
+            // and there is no tail) and the tail row
+            int n_band = mt_n / kRowBlock;
+            int last_rows = mt_n - n_band * kRowBlock;
+            if (last_rows == 0 && !tail) {
+                n_band -= 1;
+                last_rows = kRowBlock;
+            }
+            int b, lb, nr, th;
+            if (L < n_band * kRowBlock * NT) {
+                b = L / (kRowBlock * NT);
+                lb = L - b * kRowBlock * NT;
+                nr = kRowBlock;
+                th = 0;
+            } else {
+                b = n_band;
+                lb = L - n_band * kRowBlock * NT;
+                nr = last_rows;
+                th = tail;
+            }
+            // pair p of the band: its nr x (1 or 2) full-row tiles, rows
+            // fastest, then its tail tile (the last pair holds one column
+            // tile when NT is odd)
+            const int per_pair = 2 * nr + th;
+            const int p = tile_min(lb / per_pair, NTP - 1);
+            const int r = lb - p * per_pair;
+            const int n_cols = tile_min(2, NT - 2 * p);
             g.e = e;
-            if (r < mt_n * n_cols) {
-                const int b = r / (n_cols * kRowBlock);
-                const int w = r - b * n_cols * kRowBlock;
-                const int nb = tile_min(kRowBlock, mt_n - b * kRowBlock);  // row tiles in the block
-                g.col0 = (c_first + w / nb) * BN;
-                g.row0 = o0 + (b * kRowBlock + w % nb) * kBM;
+            if (r < nr * n_cols) {
+                g.col0 = (2 * p + r / nr) * BN;
+                g.row0 = o0 + (b * kRowBlock + r % nr) * kBM;
             } else {
                 g.is_tail = true;
-                g.col0 = (c_first + 2 * (r - mt_n * n_cols)) * BN;
+                g.col0 = 2 * p * BN;
                 g.row0 = o0 + (n_e >> 8) * kBM;
             }
             g.row_end = o0 + n_e;

@@ -4,8 +4,10 @@
 // tile an expert needs (its full-row tiles in every column tile, and one tail
 // tile per pair of column tiles when 1..128 rows remain past its last
 // multiple of 256) is covered.  Also checks the round shape the order is
-// for: the first 32 tiles of an expert of >= 8 row tiles and >= 4 column
-// tiles are 8 row tiles x 4 column tiles.  Prints "ok" and exits 0 on success.
+// for: on an expert of 20 row tiles and 12 column tiles, each run of 32
+// tiles of its first band that starts at a column boundary is 8 row tiles x
+// 4 column tiles, the same 8 row tiles in every run, and any other run of
+// 32 in the band spans those 8 row tiles and 5 column tiles.  Prints "ok" and exits 0 on success.
 #include <cstdio>
 #include <random>
 #include <set>
@@ -84,18 +86,25 @@ int main() {
         }
         if (check_one(off, E, NT, trial % 2 ? 128 : 256, &checked)) return 1;
     }
-    // round shape: an expert of 20 row tiles, 12 column tiles
+    // round shape: an expert of 20 row tiles, 12 column tiles (first band:
+    // tiles 0..95, rows 0..7)
     const int32_t off[2] = {0, 20 * 256};
-    std::set<int> rows, cols;
-    for (int t = 0; t < 32; ++t) {
-        const TileGeo g = moe::tile_geometry(t, off, 1, 12, 6, 128);
-        rows.insert(g.row0 / 256);
-        cols.insert(g.col0 / 128);
-    }
-    if (rows.size() != 8 || cols.size() != 4) {
-        std::printf("first 32 tiles span %zu row tiles x %zu column tiles, expected 8 x 4\n",
-                    rows.size(), cols.size());
-        return 1;
+    for (int start : {0, 32, 64, 16, 4, 20, 44}) {
+        std::set<int> rows, cols;
+        for (int t = start; t < start + 32; ++t) {
+            const TileGeo g = moe::tile_geometry(t, off, 1, 12, 6, 128);
+            rows.insert(g.row0 / 256);
+            cols.insert(g.col0 / 128);
+        }
+        // (a run that starts part way through a column ends part way
+        // through its fifth)
+        const size_t want_cols = start % 8 ? 5 : 4;
+        if (rows.size() != 8 || *rows.begin() != 0 || *rows.rbegin() != 7 ||
+            cols.size() != want_cols) {
+            std::printf("tiles %d..%d span %zu row tiles x %zu column tiles, expected rows 0..7 x %zu\n",
+                        start, start + 31, rows.size(), cols.size(), want_cols);
+            return 1;
+        }
     }
     std::printf("ok: %ld tiles checked\n", checked);
     return 0;

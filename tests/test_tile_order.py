@@ -1,6 +1,6 @@
 """The tile GEMMs' tile numbering (csrc/tile_order.h), built for the host and
 checked on the CPU: every tile covered exactly once, and rounds of 8 row tiles
-x 4 column tiles on experts with many rows."""
+x 4 column tiles, bands keeping their 8 row tiles, on experts with many rows."""
 import os
 import subprocess
 
