@@ -353,11 +353,14 @@ def mixtral_weights():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 64, 128, 191])
 def test_mixtral_shape_small_batches(T, mixtral_weights):
     """The batch sizes at the HBM-bound end of the batch sweep, at d=4096,
     f=14336, E=8, k=2, every token: the streamed kernels with GEMM 1's K
-    split over the waves and GEMM 2 cut into up to 13 K slices (T = 1)."""
+    split over the waves (T <= 2), GEMM 2 cut into up to 13 K slices (T = 1),
+    and row tiles of 1, 2 and 4 fragments over the full K loops (about 16,
+    32 and 48 rows per expert at T = 64, 128 and 191, the largest batch on
+    the streamed path, where experts past 64 rows take a second tile)."""
     w, host_w = mixtral_weights
     banner("Mixtral shape T=%d (all tokens)" % T)
     inp = dict(w)
