@@ -38,15 +38,15 @@ def test_tiny_fp32_workload():
 
 SMALL = [
     # T, d, f, E, k, dtype
-    (300, 192, 320, 8, 2, torch.bfloat16),    # 128-row tiles, ragged rows and columns
-    (40, 256, 384, 8, 2, torch.bfloat16),     # 32-row tiles
+    (300, 192, 320, 8, 2, torch.bfloat16),    # 256-row tiles: tail tiles only (~75 rows per expert), ragged
+    (40, 256, 384, 8, 2, torch.bfloat16),     # streamed, one-fragment tiles
     (1, 128, 128, 8, 2, torch.bfloat16),      # one token
     (257, 512, 640, 6, 3, torch.bfloat16),
     (100, 128, 192, 4, 1, torch.bfloat16),    # k = 1
     (64, 128, 128, 4, 4, torch.bfloat16),     # k = E: dense softmax mixture
     (33, 64, 128, 1, 1, torch.bfloat16),      # E = 1: plain SwiGLU
     (100, 128, 128, 64, 8, torch.bfloat16),   # widest routing
-    (700, 256, 256, 8, 2, torch.bfloat16),    # several 128-row tiles per expert
+    (700, 256, 256, 8, 2, torch.bfloat16),    # 256-row tiles: one partial row tile per expert (~175 rows)
     # 256x256 macro tiles (at least 128 rows per expert on average)
     (1100, 256, 384, 8, 2, torch.bfloat16),   # partial last row tiles, K split 2 in GEMM 2
     (600, 192, 320, 4, 2, torch.bfloat16),    # ragged columns in both GEMMs
@@ -59,7 +59,7 @@ SMALL = [
     (2, 256, 1024, 8, 2, torch.bfloat16),     # GEMM 1 with K split over the waves
     (110, 192, 320, 8, 2, torch.bfloat16),    # streamed, 2 row fragments per tile, ragged slabs
     (150, 256, 512, 8, 2, torch.bfloat16),    # streamed, 4 row fragments per tile
-    (200, 256, 512, 8, 2, torch.bfloat16),    # 256-row tiles: tail tiles only, GEMM 2 tiles cut in 2 K pieces
+    (200, 256, 512, 8, 2, torch.bfloat16),    # 256-row tiles: tail tiles only (~50 rows per expert)
     (600, 512, 1024, 8, 2, torch.bfloat16),   # GEMM 2's last round cut into 4 K pieces (fixup sums them)
     (1500, 1024, 2048, 8, 2, torch.bfloat16), # GEMM 2 tiles cut into 3 K pieces, several per XCD
     (2600, 768, 704, 2, 2, torch.bfloat16),   # 10 row tiles + a tail per expert: a partial block of
@@ -101,6 +101,7 @@ def test_small_shapes(T, d, f, E, k, dtype):
 CUT_CASES = [
     # T, d, f, E, k, piece counts GEMM 2's schedule cuts tiles into (E = 1 or
     # k = E: every expert's row count is known, so the tile plan is)
+    (256, 256, 512, 1, 1, {2}),
     (256, 2048, 2048, 1, 1, {8}),
     (256, 2048, 1536, 1, 1, {6}),
     (256, 2048, 1280, 1, 1, {5}),
@@ -111,9 +112,9 @@ CUT_CASES = [
 
 @pytest.mark.parametrize("T,d,f,E,k,pieces", CUT_CASES)
 def test_gemm2_tiles_cut_into_k_pieces(T, d, f, E, k, pieces):
-    """GEMM 2's last round cut into 5, 6 or 8 K pieces (the counts the
-    full-size workloads use), the fixup summing them: every row of out, h
-    and y against the oracle."""
+    """GEMM 2's last round cut into 2, 4, 5, 6 or 8 K pieces (5, 6 and 8 are
+    the counts the full-size workloads use), the fixup summing them: every
+    row of out, h and y against the oracle."""
     import tile_plan
     cpx = torch.cuda.get_device_properties(0).multi_processor_count // 8
     assert tile_plan.gemm2_pieces([T * k // E] * E, d, f, cpx) == pieces
