@@ -145,7 +145,7 @@ moe_status_t moe_ffn_forward_ex(const void *x, const void *w_router, const void 
  * NULL: bf16, no options); opts->workspace must be NULL.  Sizes whose
  * workspace (moe_ffn_workspace_bytes) exceeds 64 MiB return
  * MOE_ERR_UNSUPPORTED before any launch; at d = 4096, f = 14336, E = 8,
- * k = 2 that admits every batch up to T = 191 tokens (the streamed-weight
+ * k = 2 that admits every batch up to T = 207 tokens (the streamed-weight
  * path).  Nothing in the scratch needs to start zeroed.  Every call on one
  * GPU uses that GPU's one array: calls that overlap on a GPU (several host
  * threads, or streams that run concurrently) race and give undefined

@@ -64,10 +64,14 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
         const int64_t busy_experts = R < E ? R : E;
         const bool tile_ok = R * (d > f ? d : f) * 2 < ((int64_t)1 << 31) &&
                              d * f * 2 < ((int64_t)1 << 31);
-        if (R < 48 * E) {
-            // Under ~48 rows per expert: stream the weights, in row tiles of
+        if (R < 52 * E) {
+            // Under 52 rows per expert: stream the weights, in row tiles of
             // up to 64 rows (1, 2 or 4 fragments of 16, chosen per tile on the
-            // device from the expert's row count).
+            // device from the expert's row count).  Measured at Mixtral
+            // shapes: 0.485 ms against 0.570 for the 256-row tiles at 48
+            // rows per expert, 0.483 against 0.583 at 52; at 56 routing
+            // spread puts experts past 64 rows (a second tile re-reads their
+            // weights) and the tiles win, 0.584 against 0.619.
             p.variant = GEMM_STREAM;
             // GEMM 1 gives each wave a 128-column slab over all of K; when
             // that leaves most CUs idle (one or two tokens), split K over the

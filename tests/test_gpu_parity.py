@@ -59,7 +59,7 @@ SMALL = [
     (2, 256, 1024, 8, 2, torch.bfloat16),     # GEMM 1 with K split over the waves
     (110, 192, 320, 8, 2, torch.bfloat16),    # streamed, 2 row fragments per tile, ragged slabs
     (150, 256, 512, 8, 2, torch.bfloat16),    # streamed, 4 row fragments per tile
-    (200, 256, 512, 8, 2, torch.bfloat16),    # 256-row tiles: tail tiles only (~50 rows per expert)
+    (240, 256, 512, 8, 2, torch.bfloat16),    # 256-row tiles: tail tiles only (~60 rows per expert)
     (600, 512, 1024, 8, 2, torch.bfloat16),   # GEMM 2's last round cut into 4 K pieces (fixup sums them)
     (1500, 1024, 2048, 8, 2, torch.bfloat16), # GEMM 2 tiles cut into 3 K pieces, several per XCD
     (2600, 768, 704, 2, 2, torch.bfloat16),   # 10 row tiles + a tail per expert: a partial block of
@@ -354,13 +354,13 @@ def mixtral_weights():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 64, 128, 191])
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 64, 128, 207])
 def test_mixtral_shape_small_batches(T, mixtral_weights):
     """The batch sizes at the HBM-bound end of the batch sweep, at d=4096,
     f=14336, E=8, k=2, every token: the streamed kernels with GEMM 1's K
     split over the waves (T <= 2), GEMM 2 cut into up to 13 K slices (T = 1),
     and row tiles of 1, 2 and 4 fragments over the full K loops (about 16,
-    32 and 48 rows per expert at T = 64, 128 and 191, the largest batch on
+    32 and 52 rows per expert at T = 64, 128 and 207, the largest batch on
     the streamed path, where experts past 64 rows take a second tile)."""
     w, host_w = mixtral_weights
     banner("Mixtral shape T=%d (all tokens)" % T)
