@@ -39,13 +39,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_select_amd", "csrc")
 # The w1/w3 grouped GEMM that runs for each workload: the streamed-weight
-# kernel at a few rows per expert, the 256x256 tile kernel at >= 128 rows per
-# expert.  Patterns match both the demangled and the mangled kernel name.
+# kernel at a few rows per expert, the 256x256 tile kernel (its weight DMA
+# not marked nontemporal at these sizes) at hundreds of rows per expert.
+# Patterns match both the demangled and the mangled kernel name.
 GEMM1_KERNEL = {
     "decode": ("gemm_stream.hip", r"stream_gemm_kernel(<true, false|ILb1ELb0E)"),
-    "prefill": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
-    "skewed": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
-    "stack": ("gemm_tile.hip", r"tile_gemm_kernel(<true>|ILb1E)"),
+    "prefill": ("gemm_tile.hip", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
+    "skewed": ("gemm_tile.hip", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
+    "stack": ("gemm_tile.hip", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
 }
 CALIBRATION_BYTES = 1 << 30
 # Profiling commands behind the committed summaries; {out} is the rocprofv3

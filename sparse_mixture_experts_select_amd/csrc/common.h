@@ -82,9 +82,11 @@ hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* off
 // stores y; launch_gemm2_tile makes both launches.
 // kb: A (x_perm) and the h output in the K-blocked layout
 size_t tile_partials_bytes(int R, int E, int d, int f);
+// nt_weights: mark the w1/w3 DMA nontemporal (each weight panel read by one
+// row tile: at up to ~192 rows per expert; GEMM 2's weight DMA always is).
 hipError_t launch_gemm1_swiglu_tile(const void* x_perm, const void* w1, const void* w3,
                                     const int32_t* offsets, int R, int E, int d, int f, int kb,
-                                    float* partials, void* h, hipStream_t stream);
+                                    float* partials, bool nt_weights, void* h, hipStream_t stream);
 // kb: A (h) in the K-blocked layout; y [R, d] fp32 (one slice)
 hipError_t launch_gemm2_tile(const void* h, const void* w2, const int32_t* offsets, int R, int E,
                              int f, int d, int kb, float* partials, float* y, hipStream_t stream);

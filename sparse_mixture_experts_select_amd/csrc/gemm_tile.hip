@@ -193,7 +193,11 @@ __device__ __forceinline__ void tile_epilogue(const floatx4 (&acc)[8][8], const 
     }
 }
 
-template <bool DUAL>
+// NT_B: the weight DMA marked nontemporal -- for launches whose weight
+// panels are each read by one row tile (GEMM 2, and GEMM 1 at up to ~192
+// rows per expert), where HBM then serves the stream faster; where several
+// row tiles share a panel through L2 the hint costs GEMM 1 6-11%.
+template <bool DUAL, bool NT_B>
 __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     const bf16* __restrict__ A, const bf16* __restrict__ B0, const bf16* __restrict__ B1,
     void* __restrict__ C, float* __restrict__ partials, const int32_t* __restrict__ offsets, int R,
@@ -344,7 +348,8 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         _Pragma("unroll") for (int i_ = 0; i_ < (NB_); ++i_)                                \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(                                       \
                 (DUAL ? ((i_ >> 1) & 1) : 0) ? b_rsrc1 : b_rsrc0,                            \
-                (lds_void*)(sb_ + (BOFF_) + 4096 * i_), 16, b_voff[i_], kb_, 0, 0);         \
+                (lds_void*)(sb_ + (BOFF_) + 4096 * i_), 16, b_voff[i_], kb_, 0,             \
+                NT_B ? 2 : 0);                                                              \
     } while (0)
 
 #define MOE_READ_A(ARR_, M_)                                                                \
@@ -582,7 +587,7 @@ int cus_per_xcd() {
     return c;
 }
 
-template <bool DUAL>
+template <bool DUAL, bool NT_B>
 hipError_t launch_tile(const void* A, const void* B0, const void* B1, void* C, float* partials,
                        const int32_t* offsets, int R, int E, int K, int N, int kb,
                        hipStream_t stream) {
@@ -600,7 +605,7 @@ hipError_t launch_tile(const void* A, const void* B0, const void* B1, void* C, f
     // tiles may be cut (a workgroup past the XCD's items exits at once, but
     // still waits for a free CU: its LDS is a whole CU's)
     const long long grid = 8 * ((n_max + 7) / 8 + (max_pieces > 1 ? 2 * cpx : 0));
-    hipLaunchKernelGGL((tile_gemm_kernel<DUAL>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((tile_gemm_kernel<DUAL, NT_B>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const bf16*>(A), reinterpret_cast<const bf16*>(B0),
                        reinterpret_cast<const bf16*>(B1), C, partials, offsets, R, E, K, N, cpx, max_pieces, kb);
     hipError_t err = hipGetLastError();
@@ -637,13 +642,16 @@ size_t tile_partials_bytes(int R, int E, int d, int f) {
 
 hipError_t launch_gemm1_swiglu_tile(const void* x_perm, const void* w1, const void* w3,
                                     const int32_t* offsets, int R, int E, int d, int f, int kb,
-                                    float* partials, void* h, hipStream_t stream) {
-    return launch_tile<true>(x_perm, w1, w3, h, partials, offsets, R, E, d, f, kb, stream);
+                                    float* partials, bool nt_weights, void* h,
+                                    hipStream_t stream) {
+    if (nt_weights)
+        return launch_tile<true, true>(x_perm, w1, w3, h, partials, offsets, R, E, d, f, kb, stream);
+    return launch_tile<true, false>(x_perm, w1, w3, h, partials, offsets, R, E, d, f, kb, stream);
 }
 
 hipError_t launch_gemm2_tile(const void* h, const void* w2, const int32_t* offsets, int R, int E,
                              int f, int d, int kb, float* partials, float* y, hipStream_t stream) {
-    return launch_tile<false>(h, w2, nullptr, y, partials, offsets, R, E, f, d, kb, stream);
+    return launch_tile<false, true>(h, w2, nullptr, y, partials, offsets, R, E, f, d, kb, stream);
 }
 
 }  // namespace moe
