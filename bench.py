@@ -154,7 +154,7 @@ def source_digest(workload):
     figures still apply."""
     h = hashlib.sha256()
     src = GEMM1_KERNEL[workload][0]
-    headers = ("common.h", "tile_order.h") if src == "gemm_tile.hip" else ("common.h",)
+    headers = ("common.h", "tile_order.h", "tile_gemm.h") if src == "gemm_tile.hip" else ("common.h",)
     for name in (src,) + headers:
         with open(os.path.join(CSRC, name), "rb") as fh:
             h.update(fh.read())

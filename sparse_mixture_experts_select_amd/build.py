@@ -19,7 +19,7 @@ LIB_NAME = "libmoe_ffn.so"
 LIB_PATH = os.path.join(BUILD_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["router.hip", "route_permute.hip", "gemm_bf16.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_f32.hip", "combine.hip", "probe.hip", "api.hip"]
+SOURCES = ["router.hip", "route_permute.hip", "gemm_bf16.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_tile_nt.hip", "gemm_f32.hip", "combine.hip", "probe.hip", "api.hip"]
 
 
 def hipcc() -> str:

@@ -360,7 +360,7 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
            "route_scan");
     mark(2);
     // The 256-row tile GEMMs read x_perm and h in a K-blocked layout (see
-    // gemm_tile.hip); a caller asking for h gets it row-major instead.
+    // tile_gemm.h); a caller asking for h gets it row-major instead.
     const int kb = (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_TILE256 && !(opts && opts->h_out)) ? 1 : 0;
     // The streamed GEMM 1 reads x through row_token itself.
     const bool gather = !(dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM);

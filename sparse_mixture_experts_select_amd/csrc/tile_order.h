@@ -1,5 +1,5 @@
 // tile_order.h -- the numbering of the 256-row macro tiles of the tile GEMMs
-// (gemm_tile.hip): which expert, rows and column tile tile number t covers,
+// (tile_gemm.h): which expert, rows and column tile tile number t covers,
 // from the per-expert row offsets alone.
 //
 // Tiles are numbered by expert, then bands of kRowBlock full row tiles (the
