@@ -44,9 +44,9 @@ CSRC = os.path.join(ROOT, "sparse_mixture_experts_select_amd", "csrc")
 # Patterns match both the demangled and the mangled kernel name.
 GEMM1_KERNEL = {
     "decode": ("gemm_stream.hip", r"stream_gemm_kernel(<true, false|ILb1ELb0E)"),
-    "prefill": ("gemm_tile.hip", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
-    "skewed": ("gemm_tile.hip", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
-    "stack": ("gemm_tile.hip", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
+    "prefill": ("tile_gemm.h", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
+    "skewed": ("tile_gemm.h", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
+    "stack": ("tile_gemm.h", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
 }
 CALIBRATION_BYTES = 1 << 30
 # Profiling commands behind the committed summaries; {out} is the rocprofv3
@@ -154,7 +154,7 @@ def source_digest(workload):
     figures still apply."""
     h = hashlib.sha256()
     src = GEMM1_KERNEL[workload][0]
-    headers = ("common.h", "tile_order.h", "tile_gemm.h") if src == "gemm_tile.hip" else ("common.h",)
+    headers = ("common.h", "tile_order.h", "gemm_tile.hip") if src == "tile_gemm.h" else ("common.h",)
     for name in (src,) + headers:
         with open(os.path.join(CSRC, name), "rb") as fh:
             h.update(fh.read())
