@@ -592,6 +592,61 @@ def mfma_probe(torch, binding, ms_target=150.0):
             "clock_ghz": round(best[1], 3)}
 
 
+def vendor_gemm(torch, wl, counts, ours, reps=10):
+    """The tile GEMMs' per-expert products run by torch.matmul (hipBLASLt on
+    this system), for context beside the library's own stage times: GEMM 1
+    as X_e [n_e, d] . [w1_e | w3_e] [d, 2f] (no SwiGLU, bf16 out) and GEMM 2
+    as H_e [n_e, f] . w2_e [f, d] (bf16 out, where the library writes fp32),
+    expert after expert, on random bf16 operands with the workload's
+    per-expert row counts.  Each is timed with the weights in the layer's
+    layout (n contiguous) and k contiguous (the layout of nn.Linear's
+    weight).  Nothing in the layer calls it."""
+    d, f = wl.d, wl.f
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    rows = [int(c) for c in counts if c > 0]
+    out = {"what": "torch.matmul (hipBLASLt) bf16 on each expert's rows in turn: gemm1 = "
+                   "x_e . [w1_e | w3_e] without the SwiGLU, gemm2 = h_e . w2_e; weights in the "
+                   "layer's layout (n contiguous) and k contiguous; random operands",
+           "rows_per_expert": rows}
+    for gemm, kdim, ndim in (("gemm1", d, 2 * f), ("gemm2", f, d)):
+        xs = [torch.randn(n, kdim, device="cuda", dtype=torch.bfloat16, generator=gen) for n in rows]
+        ws = [torch.randn(kdim, ndim, device="cuda", dtype=torch.bfloat16, generator=gen)
+              for _ in rows]
+        flops = 2.0 * sum(rows) * kdim * ndim
+        vendor = {}
+        for layout in ("n_contiguous", "k_contiguous"):
+            if layout == "k_contiguous":
+                ws = [w.t().contiguous().t() for w in ws]  # same values, k fastest
+
+            def run():
+                for x, w in zip(xs, ws):
+                    torch.matmul(x, w)
+
+            for _ in range(3):
+                run()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                run()
+            b.record()
+            torch.cuda.synchronize()
+            vendor[layout] = round(a.elapsed_time(b) / reps, 5)
+        del xs, ws
+        torch.cuda.empty_cache()
+        out[gemm] = {
+            "ours_ms": ours[gemm], "ours_tflops": round(flops / (ours[gemm] * 1e-3) / 1e12, 1),
+            "torch_matmul_ms": vendor,
+            "torch_matmul_tflops": {kk: round(flops / (v * 1e-3) / 1e12, 1) for kk, v in vendor.items()},
+            "vendor_ms_over_ours": {kk: round(v / ours[gemm], 4) for kk, v in vendor.items()},
+        }
+        log("[bench] vendor %s (%s rows): ours %.4f ms, torch.matmul %.4f ms (n-contiguous "
+            "weights), %.4f ms (k-contiguous)" % (gemm, wl.name, ours[gemm], vendor["n_contiguous"],
+                                                 vendor["k_contiguous"]))
+    return out
+
+
 def calibrate_copy(torch, nbytes=CALIBRATION_BYTES, reps=3):
     """Plain device-to-device copies of a known size (reference for the
     FETCH_SIZE / WRITE_SIZE counters)."""
@@ -833,6 +888,9 @@ def main():
                     help="also time the 32-block stack (90 GB of weights resident)")
     ap.add_argument("--sweep", default="on", choices=["on", "off"],
                     help="also time the layer over T = 1 .. 16384 (prefill weights)")
+    ap.add_argument("--vendor", default="on", choices=["on", "off"],
+                    help="time torch.matmul (hipBLASLt) on the prefill workload's per-expert "
+                         "GEMM shapes beside the library's GEMM stages")
     ap.add_argument("--sweep-steps", type=int, default=5,
                     help="timed steps per batch size in the sweep")
     ap.add_argument("--cpu-full", nargs="+", default=["tiny", "prefill"],
@@ -905,6 +963,8 @@ def main():
         "note": ("each step streams the expert weights from HBM: one layer's 2.82 GB exceeds the "
                  "256 MiB MALL, so no cache flush is needed between steps"),
     }
+    side_counts = {}
+
     def side_workload(name):
         # free the primary inputs while another workload runs
         prim_inp = prim.pop("inp")
@@ -913,6 +973,7 @@ def main():
         res.pop("inp")
         torch.cuda.empty_cache()
         prim["inp"] = prim_inp
+        side_counts[name] = res["counts"]
         out = {
             "workload": name, "value": round(res["tokens_per_s"], 1), "unit": "tokens/s",
             "ms_per_step": round(res["ms_per_step"], 5),
@@ -935,6 +996,14 @@ def main():
         rec["secondary"] = side_workload(args.secondary)
     if args.skewed == "on" and args.workload != "skewed" and args.secondary != "skewed":
         rec["skewed"] = side_workload("skewed")
+    if args.vendor == "on" and "prefill" in (args.workload, args.secondary):
+        pre = rec["stages_ms"] if args.workload == "prefill" else rec["secondary"]["stages_ms"]
+        counts = prim["counts"] if args.workload == "prefill" else side_counts["prefill"]
+        prim_inp = prim.pop("inp")
+        torch.cuda.empty_cache()
+        rec["vendor_gemm"] = vendor_gemm(torch, inputs.WORKLOADS["prefill"], counts,
+                                         {"gemm1": pre["gemm1_swiglu"], "gemm2": pre["gemm2"]})
+        prim["inp"] = prim_inp
     if args.sweep == "on":
         prim_inp = prim.pop("inp")
         del prim_inp
