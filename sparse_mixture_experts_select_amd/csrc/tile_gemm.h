@@ -21,7 +21,10 @@
 // step (40 KiB against 32 KiB for a full tile) and covers two column tiles,
 // where a 256-row tile would spend a full tile's loads and MFMAs per column
 // tile on rows that do not exist.  The kernel is data-movement bound, so a
-// tail tile costs about 1.25 full tiles for the work of two.
+// tail tile costs about 1.25 full tiles for the work of two.  Its waves all
+// hold the same rows, so a tail tile multiplies only the 16-row fragments
+// that hold some of them (2 up to 32 rows, 4 up to 64, else all 8): each
+// fragment count is its own expansion of the K loop, chosen per tile.
 //
 // Staging: global -> LDS by DMA (buffer_load_dwordx4 ... lds: lane l's 16
 // bytes land at the wave's LDS base + 16 l).  SGPR buffer descriptors over A
@@ -366,8 +369,8 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)((ST_) + b_frag[N_] + 4 * 256)), \
         0, 1, 2, 3, 4, 5, 6, 7))
 
-#define MOE_MFMAS(N_, BF_)                                                                  \
-    _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_)                                        \
+#define MOE_MFMAS(N_, BF_, MF_)                                                             \
+    _Pragma("unroll") for (int m_ = 0; m_ < (MF_); ++m_)                                    \
         acc[m_][N_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m_], BF_, acc[m_][N_], 0, 0, 0)
 
 // Scheduling hints: within a group of 8 MFMAs, put one of the group's LDS
@@ -396,24 +399,26 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     // and issues its (repeated, never read) refill, so every path through the
     // loop issues the same sequence of DMA loads: the compiler's DMA wait
     // tracking then stays per stage across the guards' control-flow merges.
-#define MOE_STEP(CUR_, NXT_, REF_, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                     \
+#define MOE_STEP(CUR_, NXT_, REF_, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)                \
     {                                                                                       \
         const lds_char* st_ = (const lds_char*)(lds_void*)(CUR_);                           \
         const bool live_ = kt < kt1;                                                        \
         bf16x8 b4_, b5_;                                                                    \
         if (live_) {                                                                        \
             const bf16x8 b2_ = MOE_READ_B(st_, 2);                                          \
-            MOE_MFMAS(0, bq0);                                                              \
+            MOE_MFMAS(0, bq0, MF_);                                                         \
             const bf16x8 b3_ = MOE_READ_B(st_, 3);                                          \
-            MOE_MFMAS(1, bq1);                                                              \
+            MOE_MFMAS(1, bq1, MF_);                                                         \
             b4_ = MOE_READ_B(st_, 4);                                                       \
-            MOE_MFMAS(2, b2_);                                                              \
+            MOE_MFMAS(2, b2_, MF_);                                                         \
             b5_ = MOE_READ_B(st_, 5);                                                       \
-            MOE_MFMAS(3, b3_);                                                              \
-            MOE_SCHED_GROUP(2, 0);                                                          \
-            MOE_SCHED_GROUP(2, 0);                                                          \
-            MOE_SCHED_GROUP(2, 0);                                                          \
-            MOE_SCHED_GROUP(2, 0);                                                          \
+            MOE_MFMAS(3, b3_, MF_);                                                         \
+            if constexpr ((MF_) == 8) {                                                     \
+                MOE_SCHED_GROUP(2, 0);                                                      \
+                MOE_SCHED_GROUP(2, 0);                                                      \
+                MOE_SCHED_GROUP(2, 0);                                                      \
+                MOE_SCHED_GROUP(2, 0);                                                      \
+            }                                                                               \
         }                                                                                   \
         MOE_WAIT_VM((NA_) + (NB_));                                                         \
         stage_barrier();                                                                    \
@@ -422,26 +427,28 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
             const lds_char* sn_ = (const lds_char*)(lds_void*)(NXT_);                       \
             bf16x8 an[8];                                                                   \
             const bf16x8 b6_ = MOE_READ_B(st_, 6);                                          \
-            an[0] = MOE_READ_A(NXT_, 0);                                                    \
-            an[1] = MOE_READ_A(NXT_, 1);                                                    \
-            MOE_MFMAS(4, b4_);                                                              \
+            if constexpr (0 < (MF_)) an[0] = MOE_READ_A(NXT_, 0);                           \
+            if constexpr (1 < (MF_)) an[1] = MOE_READ_A(NXT_, 1);                           \
+            MOE_MFMAS(4, b4_, MF_);                                                         \
             const bf16x8 b7_ = MOE_READ_B(st_, 7);                                          \
-            an[2] = MOE_READ_A(NXT_, 2);                                                    \
-            an[3] = MOE_READ_A(NXT_, 3);                                                    \
-            MOE_MFMAS(5, b5_);                                                              \
-            an[4] = MOE_READ_A(NXT_, 4);                                                    \
-            an[5] = MOE_READ_A(NXT_, 5);                                                    \
-            an[6] = MOE_READ_A(NXT_, 6);                                                    \
-            an[7] = MOE_READ_A(NXT_, 7);                                                    \
+            if constexpr (2 < (MF_)) an[2] = MOE_READ_A(NXT_, 2);                           \
+            if constexpr (3 < (MF_)) an[3] = MOE_READ_A(NXT_, 3);                           \
+            MOE_MFMAS(5, b5_, MF_);                                                         \
+            if constexpr (4 < (MF_)) an[4] = MOE_READ_A(NXT_, 4);                           \
+            if constexpr (5 < (MF_)) an[5] = MOE_READ_A(NXT_, 5);                           \
+            if constexpr (6 < (MF_)) an[6] = MOE_READ_A(NXT_, 6);                           \
+            if constexpr (7 < (MF_)) an[7] = MOE_READ_A(NXT_, 7);                           \
             bq0 = MOE_READ_B(sn_, 0);                                                       \
-            MOE_MFMAS(6, b6_);                                                              \
+            MOE_MFMAS(6, b6_, MF_);                                                         \
             bq1 = MOE_READ_B(sn_, 1);                                                       \
-            MOE_MFMAS(7, b7_);                                                              \
-            MOE_SCHED_GROUP(4, G4_);                                                        \
-            MOE_SCHED_GROUP(4, G5_);                                                        \
-            MOE_SCHED_GROUP(6, G6_);                                                        \
-            MOE_SCHED_GROUP(2, G7_);                                                        \
-            _Pragma("unroll") for (int m_ = 0; m_ < 8; ++m_) af[m_] = an[m_];               \
+            MOE_MFMAS(7, b7_, MF_);                                                         \
+            if constexpr ((MF_) == 8) {                                                     \
+                MOE_SCHED_GROUP(4, G4_);                                                    \
+                MOE_SCHED_GROUP(4, G5_);                                                    \
+                MOE_SCHED_GROUP(6, G6_);                                                    \
+                MOE_SCHED_GROUP(2, G7_);                                                    \
+            }                                                                               \
+            _Pragma("unroll") for (int m_ = 0; m_ < (MF_); ++m_) af[m_] = an[m_];           \
         }                                                                                   \
         ++kt;                                                                               \
     }
@@ -452,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     // exactly two younger steps are in flight and one fixed vmcnt leaves the
     // next step's loads complete.  Past the last step the refills repeat it
     // (valid addresses, never read).
-#define MOE_K_LOOP(NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                                     \
+#define MOE_K_LOOP(NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)                                \
     {                                                                                       \
         MOE_ISSUE_STAGE(kt0, st0, NA_, NB_, BOFF_);                                         \
         MOE_ISSUE_STAGE(min(kt0 + 1, kt1 - 1), st1, NA_, NB_, BOFF_);                       \
@@ -460,22 +467,31 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         MOE_WAIT_VM(2 * ((NA_) + (NB_)));                                                   \
         stage_barrier();                                                                    \
         bf16x8 af[8];                                                                       \
-        _Pragma("unroll") for (int m = 0; m < 8; ++m) af[m] = MOE_READ_A(st0, m);           \
+        _Pragma("unroll") for (int m = 0; m < (MF_); ++m) af[m] = MOE_READ_A(st0, m);       \
         const lds_char* s0_ = (const lds_char*)(lds_void*)st0;                              \
         bf16x8 bq0 = MOE_READ_B(s0_, 0);                                                    \
         bf16x8 bq1 = MOE_READ_B(s0_, 1);                                                    \
         while (kt < kt1) {                                                                  \
-            MOE_STEP(st0, st1, st3, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                    \
-            MOE_STEP(st1, st2, st0, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                    \
-            MOE_STEP(st2, st3, st1, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                    \
-            MOE_STEP(st3, st0, st2, NA_, NB_, BOFF_, G4_, G5_, G6_, G7_)                    \
+            MOE_STEP(st0, st1, st3, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)               \
+            MOE_STEP(st1, st2, st0, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)               \
+            MOE_STEP(st2, st3, st1, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)               \
+            MOE_STEP(st3, st0, st2, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)               \
         }                                                                                   \
     }
 
     int kt = kt0;
     if (kt0 < kt1) {
-        if (is_tail) MOE_K_LOOP(2, 8, kBOffTail, 3, 3, 2, 2)
-        else MOE_K_LOOP(4, 4, kBOffFull, 2, 2, 2, 2)
+        if (!is_tail) {
+            MOE_K_LOOP(4, 4, kBOffFull, 8, 2, 2, 2, 2)
+        } else {
+            // A tail tile's rows are its expert's last 1..128: only the
+            // 16-row fragments that hold some of them are multiplied (2, 4
+            // or all 8); the rest stay zero and are never stored.
+            const int tail_rows = row_end - row0;
+            if (tail_rows <= 32) MOE_K_LOOP(2, 8, kBOffTail, 2, 0, 0, 0, 0)
+            else if (tail_rows <= 64) MOE_K_LOOP(2, 8, kBOffTail, 4, 0, 0, 0, 0)
+            else MOE_K_LOOP(2, 8, kBOffTail, 8, 3, 3, 2, 2)
+        }
     }
 #undef MOE_K_LOOP
 #undef MOE_SCHED_GROUP

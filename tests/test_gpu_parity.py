@@ -125,6 +125,35 @@ def test_gemm2_tiles_cut_into_k_pieces(T, d, f, E, k, pieces):
     print("near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
 
 
+
+TAIL_CASES = [
+    # T, d, f, E, k, rows past the expert's last multiple of 256 (E = 1 or
+    # k = E: every expert holds T*k/E rows), GEMM 2's piece counts
+    (276, 2048, 2048, 1, 1, 20, {5}),   # a 256-row tile + 20-row tails (2 fragments), all cut
+    (300, 1024, 2048, 2, 2, 44, {5}),   # 44-row tails (4 fragments)
+    (60, 2048, 2048, 1, 1, 60, {8}),    # tail tiles only, 60 rows (4 fragments), cut into 8
+    (90, 1024, 2048, 2, 2, 90, {8}),    # tail tiles only, 90 rows (all 8 fragments)
+]
+
+
+@pytest.mark.parametrize("T,d,f,E,k,tail,pieces", TAIL_CASES)
+def test_tail_tiles_by_row_fragments(T, d, f, E, k, tail, pieces):
+    """Tail tiles (an expert's last 1..128 rows over two column tiles)
+    multiply only the 16-row fragments that hold rows: 2 for up to 32 rows,
+    4 for up to 64, else 8.  One case per class, in both GEMMs and in GEMM 2
+    tiles cut into K pieces (the tails among them): every row of out, h and
+    y against the oracle."""
+    import tile_plan
+    rows = T * k // E
+    assert rows % 256 == tail
+    cpx = torch.cuda.get_device_properties(0).multi_processor_count // 8
+    assert tile_plan.gemm2_pieces([rows] * E, d, f, cpx) == pieces
+    banner("tail tiles of %d rows: T=%d d=%d f=%d E=%d k=%d" % (tail, T, d, f, E, k))
+    inp = case(T, d, f, E, torch.bfloat16, seed=T + d + f + 1, label="tail")
+    r = PT.full_check(inp, k)
+    np.testing.assert_array_equal(PT.to_np(r["gpu"]["counts"]), [rows] * E)
+    print("near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
+
 def test_batch_with_h_past_2gib():
     """h = 65600 x 16384 bf16 is past 2 GiB: the GEMMs fall back from the
     256-row tile kernels (32-bit buffer offsets) to the 128-row grouped ones."""
