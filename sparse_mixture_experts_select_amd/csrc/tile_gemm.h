@@ -10,9 +10,12 @@
 //
 // Workgroup: 256 threads = 4 wavefronts in a 2x2 grid.  Macro tile: 256 rows x
 // 256 weight columns (GEMM 1: 128 columns of w1 and the same 128 of w3; GEMM 2:
-// 256 columns of w2), K step 32.  Each wave owns a 128 x 128 block of
+// 256 columns of w2), K step 32.  Each wave owns 128 rows x 128 columns of
 // accumulators (8 x 8 fragments of v_mfma_f32_16x16x32_bf16, 256 fp32 per
-// lane, held in AGPRs), so every fragment read from LDS feeds 8 MFMAs.
+// lane, held in AGPRs), so every fragment read from LDS feeds 8 MFMAs; its
+// rows are the tile's alternate 16-row fragments (wave row wm: fragments
+// wm, wm + 2, ...), so that in a tile with fewer than 256 rows both wave rows
+// can skip their empty fragments alike.
 //
 // Tail tiles.  An expert's rows past its last multiple of 256, when there are
 // at most 128 of them, form a tail tile of 128 rows x two column tiles: the
@@ -23,8 +26,9 @@
 // tile on rows that do not exist.  The kernel is data-movement bound, so a
 // tail tile costs about 1.25 full tiles for the work of two.  Its waves all
 // hold the same rows, so a tail tile multiplies only the 16-row fragments
-// that hold some of them (2 up to 32 rows, 4 up to 64, else all 8): each
-// fragment count is its own expansion of the K loop, chosen per tile.
+// that hold some of them (2 up to 32 rows, 4 up to 64, 6 up to 96, else all
+// 8), and a full tile with at most 192 rows 6 per wave: each fragment count
+// is its own expansion of the K loop, chosen per tile.
 //
 // Staging: global -> LDS by DMA (buffer_load_dwordx4 ... lds: lane l's 16
 // bytes land at the wave's LDS base + 16 l).  SGPR buffer descriptors over A
@@ -145,9 +149,10 @@ __device__ __forceinline__ void tile_epilogue(const floatx4 (&acc)[8][8], const 
     if (DUAL) {
         __syncthreads();  // every wave is done reading the stages
         // Stage the wave pair's 128 x 128 bf16 block of h in LDS (wm = 0 in
-        // st0, wm = 1 in st1; full tile: rows 0..127 | 128..255, tail tile:
-        // first | second column tile), 256 bytes per row, 16-byte chunk ch of
-        // row r stored at ch ^ (r % 16).
+        // st0, wm = 1 in st1; full tile: the wave row's alternate 16-row
+        // fragments, block row rr = tile row 32 (rr/16) + 16 wm + rr%16; tail
+        // tile: first | second column tile), 256 bytes per row, 16-byte chunk
+        // ch of row r stored at ch ^ (r % 16).
         uint16_t* hs_w = reinterpret_cast<uint16_t*>(wm == 0 ? st0 : st1);
 #pragma unroll
         for (int m = 0; m < 8; ++m)
@@ -175,7 +180,7 @@ __device__ __forceinline__ void tile_epilogue(const floatx4 (&acc)[8][8], const 
                 const int b = idx >> 10;          // block of 32 columns within the 128
                 const int ch = 4 * b + piece;     // 16-byte chunk of the staged row
                 const int rr = sr & 127;
-                const int grow = row0 + (is_tail ? rr : sr);
+                const int grow = row0 + (is_tail ? rr : 32 * (rr >> 4) + 16 * (sr >> 7) + (rr & 15));
                 const int gc = col0 + (is_tail ? (sr >> 7) * BN : 0) + ch * 8;
                 const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(sr < 128 ? st0 : st1);
                 if (grow < row_end && gc < N)
@@ -189,7 +194,7 @@ __device__ __forceinline__ void tile_epilogue(const floatx4 (&acc)[8][8], const 
                 const int sr = idx >> 4;    // 0..255
                 const int ch = idx & 15;    // 16-byte chunk of the row
                 const int rr = sr & 127;
-                const int grow = row0 + (is_tail ? rr : sr);
+                const int grow = row0 + (is_tail ? rr : 32 * (rr >> 4) + 16 * (sr >> 7) + (rr & 15));
                 const int gc = col0 + (is_tail ? (sr >> 7) * BN : 0) + ch * 8;
                 const uint16_t* hs_r = reinterpret_cast<const uint16_t*>(sr < 128 ? st0 : st1);
                 if (grow < row_end && gc < N)
@@ -314,10 +319,13 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     const int b_step = kBK * N * 2;                 // bytes per K step in B
 
     // ---- fragment addressing (bytes within a stage)
-    // A fragment m: row 16 m + lrow of this wave's 128 rows (rows wm*128.. in a
-    // full tile, the tail's 128 rows for every wave), chunk lgrp, stored at
-    // chunk lgrp ^ ((row/2)%4) = lgrp ^ ((lrow/2)%4).
-    const int a_frag = ((is_tail ? 0 : wm * 128) + lrow) * 64 + 16 * (lgrp ^ ((lrow >> 1) & 3));
+    // A fragment m: in a full tile the tile's 16-row fragment 2 m + wm (the
+    // two wave rows take alternate fragments, so a tile with fewer than 256
+    // rows leaves both about equally empty), in a tail tile fragment m of the
+    // tail's 128 rows for every wave; lane row lrow, chunk lgrp, stored at
+    // chunk lgrp ^ ((row/2)%4) = lgrp ^ ((lrow/2)%4).  Fragment m + 1 lies
+    // 32 rows (full) or 16 rows (tail) further on.
+    const int a_frag = ((is_tail ? 0 : wm * 16) + lrow) * 64 + 16 * (lgrp ^ ((lrow >> 1) & 3));
     // B fragment n: 16 columns of one block; lane (lgrp, lrow) addresses k row
     // 8 lgrp + lrow/4 (+4 for the second read), columns 4 (lrow%4) .. +3.
     const int b_k = 8 * lgrp + (lrow >> 2);
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 
 #define MOE_READ_A(ARR_, M_)                                                                \
     (*reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(                    \
-        (const lds_char*)(lds_void*)(ARR_) + a_frag + (M_) * 16 * 64))
+        (const lds_char*)(lds_void*)(ARR_) + a_frag + (M_) * a_mstride_))
 
 #define MOE_READ_B(ST_, N_)                                                                 \
     __builtin_bit_cast(bf16x8, __builtin_shufflevector(                                     \
@@ -373,15 +381,23 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     _Pragma("unroll") for (int m_ = 0; m_ < (MF_); ++m_)                                    \
         acc[m_][N_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m_], BF_, acc[m_][N_], 0, 0, 0)
 
-// Scheduling hints: within a group of 8 MFMAs, put one of the group's LDS
-// reads (for fragments two groups ahead) after each of the first NR_ MFMAs,
-// and NV_ of the stage refill's DMA loads among the later MFMAs, so the wave
-// never holds a burst of memory instructions while the matrix core idles.
+// Scheduling hints: within a group of 8 (or 6) MFMAs, put one of the group's
+// LDS reads (for fragments two groups ahead) after each of the first NR_
+// MFMAs, and NV_ of the stage refill's DMA loads among the later MFMAs, so
+// the wave never holds a burst of memory instructions while the matrix core
+// idles.  Loops of 2 or 4 fragments are left to the compiler.
 #define MOE_SCHED_GROUP(NR_, NV_)                                                           \
     _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                      \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
         if (i_ < (NR_)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  \
         if ((i_ == 2 && (NV_) > 0) || (i_ == 5 && (NV_) > 1) || (i_ == 7 && (NV_) > 2))     \
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                              \
+    }
+#define MOE_SCHED_GROUP6(NR_, NV_)                                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < 6; ++i_) {                                      \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+        if (i_ < (NR_)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  \
+        if ((i_ == 1 && (NV_) > 0) || (i_ == 4 && (NV_) > 1) || (i_ == 5 && (NV_) > 2))     \
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                              \
     }
 
@@ -418,6 +434,11 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
                 MOE_SCHED_GROUP(2, 0);                                                      \
                 MOE_SCHED_GROUP(2, 0);                                                      \
                 MOE_SCHED_GROUP(2, 0);                                                      \
+            } else if constexpr ((MF_) == 6) {                                              \
+                MOE_SCHED_GROUP6(2, 0);                                                     \
+                MOE_SCHED_GROUP6(2, 0);                                                     \
+                MOE_SCHED_GROUP6(2, 0);                                                     \
+                MOE_SCHED_GROUP6(2, 0);                                                     \
             }                                                                               \
         }                                                                                   \
         MOE_WAIT_VM((NA_) + (NB_));                                                         \
@@ -447,6 +468,11 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
                 MOE_SCHED_GROUP(4, G5_);                                                    \
                 MOE_SCHED_GROUP(6, G6_);                                                    \
                 MOE_SCHED_GROUP(2, G7_);                                                    \
+            } else if constexpr ((MF_) == 6) {                                              \
+                MOE_SCHED_GROUP6(4, G4_);                                                   \
+                MOE_SCHED_GROUP6(4, G5_);                                                   \
+                MOE_SCHED_GROUP6(4, G6_);                                                   \
+                MOE_SCHED_GROUP6(2, G7_);                                                   \
             }                                                                               \
             _Pragma("unroll") for (int m_ = 0; m_ < (MF_); ++m_) af[m_] = an[m_];           \
         }                                                                                   \
@@ -459,8 +485,9 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     // exactly two younger steps are in flight and one fixed vmcnt leaves the
     // next step's loads complete.  Past the last step the refills repeat it
     // (valid addresses, never read).
-#define MOE_K_LOOP(NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)                                \
+#define MOE_K_LOOP(NA_, NB_, BOFF_, MF_, AMS_, G4_, G5_, G6_, G7_)                          \
     {                                                                                       \
+        constexpr int a_mstride_ = (AMS_);                                                  \
         MOE_ISSUE_STAGE(kt0, st0, NA_, NB_, BOFF_);                                         \
         MOE_ISSUE_STAGE(min(kt0 + 1, kt1 - 1), st1, NA_, NB_, BOFF_);                       \
         MOE_ISSUE_STAGE(min(kt0 + 2, kt1 - 1), st2, NA_, NB_, BOFF_);                       \
@@ -481,20 +508,24 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 
     int kt = kt0;
     if (kt0 < kt1) {
+        // Only the 16-row fragments that hold some of the tile's rows are
+        // multiplied (the rest stay zero and are never stored): a tail tile
+        // (the expert's last 1..128 rows, the same rows in every wave) takes
+        // 2, 4, 6 or 8 of them, a full tile with at most 192 rows 6 per wave.
+        const int tile_rows = min(row_end - row0, 256);
         if (!is_tail) {
-            MOE_K_LOOP(4, 4, kBOffFull, 8, 2, 2, 2, 2)
+            if (tile_rows <= 192) MOE_K_LOOP(4, 4, kBOffFull, 6, 32 * 64, 2, 2, 2, 2)
+            else MOE_K_LOOP(4, 4, kBOffFull, 8, 32 * 64, 2, 2, 2, 2)
         } else {
-            // A tail tile's rows are its expert's last 1..128: only the
-            // 16-row fragments that hold some of them are multiplied (2, 4
-            // or all 8); the rest stay zero and are never stored.
-            const int tail_rows = row_end - row0;
-            if (tail_rows <= 32) MOE_K_LOOP(2, 8, kBOffTail, 2, 0, 0, 0, 0)
-            else if (tail_rows <= 64) MOE_K_LOOP(2, 8, kBOffTail, 4, 0, 0, 0, 0)
-            else MOE_K_LOOP(2, 8, kBOffTail, 8, 3, 3, 2, 2)
+            if (tile_rows <= 32) MOE_K_LOOP(2, 8, kBOffTail, 2, 16 * 64, 0, 0, 0, 0)
+            else if (tile_rows <= 64) MOE_K_LOOP(2, 8, kBOffTail, 4, 16 * 64, 0, 0, 0, 0)
+            else if (tile_rows <= 96) MOE_K_LOOP(2, 8, kBOffTail, 6, 16 * 64, 3, 3, 2, 2)
+            else MOE_K_LOOP(2, 8, kBOffTail, 8, 16 * 64, 3, 3, 2, 2)
         }
     }
 #undef MOE_K_LOOP
 #undef MOE_SCHED_GROUP
+#undef MOE_SCHED_GROUP6
 #undef MOE_MFMAS
 #undef MOE_READ_B
 #undef MOE_READ_A
@@ -540,13 +571,14 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
     // them would cost registers across it.
     const int ewave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int elane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    const int rbase = (is_tail ? 0 : (ewave >> 1) * 128) + 4 * (elane >> 4);
+    const int rbase = (is_tail ? 0 : (ewave >> 1) * 16) + 4 * (elane >> 4);
+    const int mstride = is_tail ? 16 : 32;  // tile rows from one fragment to the next
     const int cbase = (is_tail ? (ewave >> 1) * BN : 0) + (ewave & 1) * 128 + (elane & 15);
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = rbase + 16 * m + r;
+            const int row = rbase + mstride * m + r;
             if (row >= rlim) continue;
 #pragma unroll
             for (int n = 0; n < 8; ++n) {

@@ -126,30 +126,34 @@ def test_gemm2_tiles_cut_into_k_pieces(T, d, f, E, k, pieces):
 
 
 
-TAIL_CASES = [
-    # T, d, f, E, k, rows past the expert's last multiple of 256 (E = 1 or
-    # k = E: every expert holds T*k/E rows), GEMM 2's piece counts
-    (276, 2048, 2048, 1, 1, 20, {5}),   # a 256-row tile + 20-row tails (2 fragments), all cut
-    (300, 1024, 2048, 2, 2, 44, {5}),   # 44-row tails (4 fragments)
-    (60, 2048, 2048, 1, 1, 60, {8}),    # tail tiles only, 60 rows (4 fragments), cut into 8
-    (90, 1024, 2048, 2, 2, 90, {8}),    # tail tiles only, 90 rows (all 8 fragments)
+FRAGMENT_CASES = [
+    # T, d, f, E, k, GEMM 2's piece counts (E = 1 or k = E: every expert
+    # holds T*k/E rows, so which K loop each tile runs is known)
+    (276, 2048, 2048, 1, 1, {5}),   # a full tile + 20-row tails (2 fragments), all cut
+    (300, 1024, 2048, 2, 2, {5}),   # full tiles + 44-row tails (4 fragments)
+    (60, 2048, 2048, 1, 1, {8}),    # tail tiles only, 60 rows (4 fragments), cut into 8
+    (80, 2048, 2048, 1, 1, {8}),    # tail tiles only, 80 rows (6 fragments)
+    (90, 1024, 2048, 2, 2, {8}),    # tail tiles only, 90 rows (6 fragments)
+    (150, 2048, 2048, 1, 1, {8}),   # one full tile of 150 rows (6 fragments per wave row)
+    (230, 1024, 2048, 2, 2, {8}),   # one full tile of 230 rows (all 8, alternate fragments part empty)
+    (420, 2048, 2048, 1, 1, {5}),   # a whole tile + a full tile of 164 rows (6 per wave row)
 ]
 
 
-@pytest.mark.parametrize("T,d,f,E,k,tail,pieces", TAIL_CASES)
-def test_tail_tiles_by_row_fragments(T, d, f, E, k, tail, pieces):
-    """Tail tiles (an expert's last 1..128 rows over two column tiles)
-    multiply only the 16-row fragments that hold rows: 2 for up to 32 rows,
-    4 for up to 64, else 8.  One case per class, in both GEMMs and in GEMM 2
-    tiles cut into K pieces (the tails among them): every row of out, h and
-    y against the oracle."""
+@pytest.mark.parametrize("T,d,f,E,k,pieces", FRAGMENT_CASES)
+def test_tiles_by_row_fragments(T, d, f, E, k, pieces):
+    """The 256-row tile kernels multiply only the 16-row fragments that hold
+    some of a tile's rows: a tail tile (an expert's last 1..128 rows over two
+    column tiles, the same rows in every wave) 2, 4, 6 or 8 of them, a full
+    tile with at most 192 rows 6 per wave row (the wave rows take alternate
+    fragments).  Each class in both GEMMs and in GEMM 2 tiles cut into K
+    pieces: every row of out, h and y against the oracle."""
     import tile_plan
     rows = T * k // E
-    assert rows % 256 == tail
     cpx = torch.cuda.get_device_properties(0).multi_processor_count // 8
     assert tile_plan.gemm2_pieces([rows] * E, d, f, cpx) == pieces
-    banner("tail tiles of %d rows: T=%d d=%d f=%d E=%d k=%d" % (tail, T, d, f, E, k))
-    inp = case(T, d, f, E, torch.bfloat16, seed=T + d + f + 1, label="tail")
+    banner("tiles of %d rows per expert: T=%d d=%d f=%d E=%d k=%d" % (rows, T, d, f, E, k))
+    inp = case(T, d, f, E, torch.bfloat16, seed=T + d + f + 1, label="frag")
     r = PT.full_check(inp, k)
     np.testing.assert_array_equal(PT.to_np(r["gpu"]["counts"]), [rows] * E)
     print("near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
