@@ -70,6 +70,21 @@ MFMA_COMMAND = ("timeout -s KILL 150 rocprofv3 --pmc " + MFMA_COUNTERS + " --out
                 "-d {out} -o run -- python3 bench.py --workload prefill --secondary none "
                 "--steps 3 --warmup 1 --stack off --skewed off --sweep off --no-cpu-baseline")
 SIMDS = 256 * 4          # MI355X: 256 CUs x 4 SIMDs
+# Four counter passes over the prefill tile GEMMs (at most 8 SQ counters a
+# pass), summarized into the wave-state breakdown.
+STALL_PASSES = (
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
+    "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_VALU_MFMA_BUSY_CYCLES",
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE SQ_LDS_DATA_FIFO_FULL "
+    "SQ_LDS_CMD_FIFO_FULL SQ_INST_LEVEL_LDS SQ_INSTS_LDS SQ_LDS_UNALIGNED_STALL",
+    "SQ_VMEM_TA_ADDR_FIFO_FULL SQ_VMEM_TA_CMD_FIFO_FULL SQ_INST_LEVEL_VMEM SQ_INSTS_VMEM "
+    "SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_MISC SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES",
+    "SQ_INSTS_MFMA SQ_INSTS_SALU SQ_INSTS_VALU SQ_INSTS_SMEM SQ_ACTIVE_INST_SCA "
+    "SQ_INST_CYCLES_SALU SQ_WAVES SQ_CYCLES",
+)
+STALL_COMMAND = ("timeout -s KILL 90 rocprofv3 --pmc {counters} GRBM_GUI_ACTIVE --output-format csv "
+                 "-d {out} -o run -- python3 bench.py --workload prefill --secondary none --steps 3 "
+                 "--warmup 1 --stack off --skewed off --sweep off --vendor off --no-cpu-baseline")
 NOMINAL_CLOCK_HZ = 2.4e9  # the clock the 2.5 PFLOP/s figure assumes
 TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d {out} -o run -- "
                  "python3 bench.py --steps 10 --warmup 2 --sweep off --cpu-seconds 2 --cpu-full none")
@@ -788,6 +803,73 @@ def summarize_mfma(run_dir):
     log("[bench] wrote", out)
 
 
+def summarize_stalls(run_dirs):
+    """Turn the four rocprofv3 --pmc passes of STALL_COMMAND (STALL_PASSES in
+    order) into profiles/tile_gemm_prefill_wave_states.txt: for the prefill
+    w1/w3 kernel and the w2 kernel, the counters per launch and where the
+    waves' cycles go.  SQ_WAVE_CYCLES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY and
+    SQ_ACTIVE_INST_ANY count in units of 4 cycles (4 x SQ_WAVE_CYCLES comes
+    to 0.95 of SIMDs x duration x clock for these kernels, which hold one
+    wave per SIMD); SQ_VALU_MFMA_BUSY_CYCLES counts cycles (16 per
+    16x16x32 bf16 MFMA)."""
+    import re
+    import statistics
+
+    kernels = (("w1/w3 grouped GEMM + SwiGLU", GEMM1_KERNEL["prefill"][1]),
+               ("w2 grouped GEMM", r"tile_gemm_kernel(<false, true>|ILb0ELb1E)"))
+    per = {name: {} for name, _ in kernels}
+    span = {name: {} for name, _ in kernels}
+    for d in run_dirs:
+        for r in _counter_rows(d):
+            for name, pattern in kernels:
+                if re.search(pattern, r["Kernel_Name"]):
+                    key = (d, r["Dispatch_Id"])
+                    per[name].setdefault(r["Counter_Name"], {}).setdefault(key, 0.0)
+                    per[name][r["Counter_Name"]][key] += float(r["Counter_Value"])
+                    span[name][key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    out = os.path.join(ROOT, "profiles", "tile_gemm_prefill_wave_states.txt")
+    with open(out, "w") as fh:
+        fh.write("# Wave states of the 256x256 tile GEMMs, prefill workload (T=4096, d=4096, f=14336, "
+                 "E=8, k=2, bf16)\n")
+        fh.write("# kernels: %s (source %s), and GEMM 2\n" % (kernels[0][1], GEMM1_KERNEL["prefill"][0]))
+        for i, counters in enumerate(STALL_PASSES):
+            fh.write("# command (pass %d): %s\n" % (i + 1, STALL_COMMAND.format(
+                counters=counters, out=run_dirs[i] if i < len(run_dirs) else "?")))
+        fh.write("# summarized by: python3 bench.py --summarize-stalls %s\n" % " ".join(run_dirs))
+        fh.write("# counters per launch, averaged over the launches of each pass; SQ_WAVE_CYCLES, "
+                 "SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_ACTIVE_INST_ANY in units of 4 cycles\n")
+        fh.write("kernel_source_sha256_16 = %s\n" % source_digest("prefill"))
+        for name, _ in kernels:
+            c = {k: statistics.mean(v.values()) for k, v in per[name].items()}
+            if "SQ_WAVE_CYCLES" not in c or "SQ_INSTS_MFMA" not in c:
+                raise SystemExit("missing counters for %s in %s" % (name, run_dirs))
+            dur = statistics.mean(t for t in span[name].values())
+            fh.write("\n[%s]\n" % name)
+            for k in sorted(c):
+                fh.write("%s = %.4g\n" % (k, c[k]))
+            wave = 4.0 * c["SQ_WAVE_CYCLES"]
+            clock = c["GRBM_GUI_ACTIVE"] / 8 / dur
+            waves = c["SQ_WAVES"]
+            fh.write("dispatch_seconds = %.4e\n" % dur)
+            fh.write("clock_ghz_from_grbm = %.3f\n" % (clock / 1e9))
+            fh.write("wave_residency = %.3f  (4 SQ_WAVE_CYCLES / (SIMDs x duration x clock))\n"
+                     % (wave / (SIMDS * dur * clock)))
+            fh.write("mfma_busy_of_wave_cycles = %.3f\n" % (c["SQ_VALU_MFMA_BUSY_CYCLES"] / wave))
+            fh.write("waiting_on_waitcnt_or_barrier = %.3f  (SQ_WAIT_ANY / SQ_WAVE_CYCLES)\n"
+                     % (c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"]))
+            fh.write("ready_but_not_issued = %.3f  (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES: mostly the "
+                     "next MFMA waiting for the matrix core)\n" % (c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]))
+            fh.write("issuing = %.3f  (SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES)\n"
+                     % (c["SQ_ACTIVE_INST_ANY"] / c["SQ_WAVE_CYCLES"]))
+            fh.write("lds_bank_conflict_cycles_per_lds_instruction = %.4f\n"
+                     % (c["SQ_LDS_BANK_CONFLICT"] / c["SQ_INSTS_LDS"]))
+            fh.write("per wave: mfma %.0f, valu (SQ_INSTS_VALU, MFMAs included) %.0f, salu %.0f, lds %.0f, "
+                     "vmem %.0f instructions\n"
+                     % (c["SQ_INSTS_MFMA"] / waves, c["SQ_INSTS_VALU"] / waves,
+                        c["SQ_INSTS_SALU"] / waves, c["SQ_INSTS_LDS"] / waves, c["SQ_INSTS_VMEM"] / waves))
+    log("[bench] wrote", out)
+
+
 def _short_kernel_name(name):
     """Readable kernel name: the library's mangled names (plain function
     templates over bool / int / bf16 / float) are decoded by hand."""
@@ -905,6 +987,8 @@ def main():
                          "SKEWED_PMC_COMMAND or STACK_PMC_COMMAND")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--summarize-stalls", nargs=4, metavar="PMC_DIR",
+                    help="the four counter passes of STALL_COMMAND, in STALL_PASSES order")
     args = ap.parse_args()
 
     if args.summarize_counters:
@@ -915,6 +999,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_stalls:
+        summarize_stalls(args.summarize_stalls)
         return
 
     if args.gpus != 1:
