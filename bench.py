@@ -43,7 +43,7 @@ CSRC = os.path.join(ROOT, "sparse_mixture_experts_select_amd", "csrc")
 # not marked nontemporal at these sizes) at hundreds of rows per expert.
 # Patterns match both the demangled and the mangled kernel name.
 GEMM1_KERNEL = {
-    "decode": ("gemm_stream.hip", r"stream_gemm_kernel(<true, false|ILb1ELb0E)"),
+    "decode": ("gemm_stream.hip", r"stream_gemm_kernel(<true, 1>|ILb1ELi1E)"),
     "prefill": ("tile_gemm.h", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
     "skewed": ("tile_gemm.h", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),
     "stack": ("tile_gemm.h", r"tile_gemm_kernel(<true, false>|ILb1ELb0E)"),

@@ -50,7 +50,7 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 struct Plan {
     int variant = GEMM_LARGE_M;
     int splits = 1;
-    bool g1_ksplit = false;  // streamed GEMM 1: split K over the waves of a workgroup
+    int g1_k_waves = 1;  // streamed GEMM 1: waves that split K for one slab (1, 2 or 4)
     size_t ids = 0, gates = 0, counts = 0, offsets = 0, slot_row = 0, row_token = 0, scan = 0;
     size_t x_perm = 0, h = 0, y = 0, partials = 0, total = 0;
 };
@@ -79,12 +79,26 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
             // spread puts experts past 64 rows (a second tile re-reads their
             // weights) and the tiles win, 0.584 against 0.619.
             p.variant = GEMM_STREAM;
-            // GEMM 1 gives each wave a 128-column slab over all of K; when
-            // that leaves most CUs idle (one or two tokens), split K over the
-            // waves of a workgroup instead (16-row tiles).
+            // GEMM 1 gives each wave a 128-column slab over all of K.  With
+            // one or two tokens that leaves most CUs idle; then 2 or 4 waves
+            // split K for each slab (2 or 1 slabs per workgroup, 16-row
+            // tiles): the most K-split shape whose workgroups fit in one
+            // round of 256 even if every assignment reaches its own expert
+            // (a second round of a few dozen workgroups streams alone, at a
+            // fraction of the HBM rate).  Measured at Mixtral shapes: T = 1
+            // 4 waves (224 workgroups); T = 2 2 waves, GEMM 1 148 -> 116 us
+            // against 4 waves; T = 3 1 wave (2 waves: 238 against ~215 us
+            // when 6 experts hold rows).
             int64_t mt16 = (R + 15) / 16;
             if (mt16 < busy_experts) mt16 = busy_experts;
-            p.g1_ksplit = R <= 12 * E && mt16 * ((f + 511) / 512) < 128;
+            if (R <= 12 * E) {
+                for (int kw : {4, 2}) {
+                    if (mt16 * ((f + 512 / kw - 1) / (512 / kw)) <= 256) {
+                        p.g1_k_waves = kw;
+                        break;
+                    }
+                }
+            }
             // GEMM 2 gives each wave a 128-column slab, the 4 waves of a
             // workgroup 4 adjacent slabs (512 contiguous columns of every w2
             // row, as GEMM 1 reads w1 and w3), and cuts K across workgroups;
@@ -369,7 +383,7 @@ moe_status_t forward_impl(const void* x, const void* w_router, const void* w1, c
     mark(3);
     if (dtype == MOE_DTYPE_BF16 && plan.variant == GEMM_STREAM) {
         LAUNCH(launch_gemm1_swiglu_stream(x, row_token, w1, w3, offsets, R, Ei, di, fi,
-                                          plan.g1_ksplit, h, stream),
+                                          plan.g1_k_waves, h, stream),
                "gemm1_swiglu");
         mark(4);
         LAUNCH(launch_gemm2_stream(h, w2, offsets, R, Ei, fi, di, plan.splits, y, stream), "gemm2");

@@ -67,10 +67,12 @@ hipError_t launch_gemm2_f32(const void* h, const void* w2, const int32_t* offset
 // The same two contractions for batches with few rows per expert: weights are
 // streamed from HBM into registers (row tiles of up to 64 rows, in 16-row
 // fragments sized per tile on the device; 128-column slabs).
-// (reads the token rows of x through row_token: no gathered copy is needed)
+// (reads the token rows of x through row_token: no gathered copy is needed;
+// k_waves = 1, 2 or 4 waves split K for each 128-column slab, with 4, 2 or
+// 1 slabs per workgroup)
 hipError_t launch_gemm1_swiglu_stream(const void* x, const int32_t* row_token, const void* w1,
                                       const void* w3, const int32_t* offsets, int R, int E, int d,
-                                      int f, bool ksplit_waves, void* h, hipStream_t stream);
+                                      int f, int k_waves, void* h, hipStream_t stream);
 hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* offsets, int R, int E,
                                int f, int d, int splits, float* y, hipStream_t stream);
 

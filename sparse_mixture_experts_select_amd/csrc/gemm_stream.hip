@@ -9,15 +9,17 @@
 // slice).  Each tile takes MF = 1, 2 or 4 fragments of 16 rows by its own
 // row count (read from the device-side offsets), so an expert with up to 64
 // rows reads its weights once, and each weight block loaded feeds MF MFMAs.
-// Two workgroup shapes, both of 4 wavefronts:
-//   KSPLIT_WAVES: one slab, tiles of 16 rows; the 4 waves split the slice's
-//                 K range into 4 contiguous quarters and add their partial
-//                 sums in LDS once at the end (GEMM 1 when only a few
-//                 experts hold rows);
-//   otherwise:    4 adjacent slabs, one per wave, each over the slice's whole
-//                 K range (no reduction): every w row is read as 512
-//                 contiguous columns per workgroup (GEMM 1, and GEMM 2 with
-//                 its K range cut into slices across workgroups).
+// Workgroups of 4 wavefronts in three shapes, by KW, the number of waves
+// that split the slice's K range for one slab:
+//   KW = 1: 4 adjacent slabs, one per wave, each over the slice's whole K
+//           range (no reduction): every w row is read as 512 contiguous
+//           columns per workgroup (GEMM 1, and GEMM 2 with its K range cut
+//           into slices across workgroups);
+//   KW = 2: 2 adjacent slabs, two waves each on the two halves of K;
+//   KW = 4: one slab, the 4 waves on 4 contiguous quarters of K.
+// With KW > 1 (GEMM 1 when only a few experts hold rows, so that enough
+// workgroups stream) tiles hold 16 rows and the waves of a slab add their
+// partial sums in LDS once at the end.
 // GEMM 1 reads its A rows straight from the token rows of x through the
 // row -> token map (no gathered copy of x is made on this path).
 // Each wavefront streams its weight rows straight from HBM into registers:
@@ -82,7 +84,7 @@ __device__ __forceinline__ bf16x8 block_column(const uint4 (&v)[8], int c) {
 // [s0, s1) of the split.
 // a_rows: when non-null, grouped row r of A is row a_rows[r] of the A matrix
 // (GEMM 1 reading the token rows of x directly, with no gathered copy).
-template <bool DUAL, bool KSPLIT_WAVES, int MF>
+template <bool DUAL, int KW, int MF>
 __device__ __forceinline__ void stream_tile(const bf16* __restrict__ A,
                                             const int32_t* __restrict__ a_rows,
                                             const bf16* __restrict__ B0,
@@ -91,17 +93,19 @@ __device__ __forceinline__ void stream_tile(const bf16* __restrict__ A,
                                             int split, int s0, int s1, int R, int K, int N,
                                             floatx4 (*red)[64]) {
     constexpr int NMAT = DUAL ? 2 : 1;
-    constexpr int TILE_N = KSPLIT_WAVES ? kSlab : 4 * kSlab;
+    constexpr int TILE_N = (4 / KW) * kSlab;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;
     const int j = lane & 15;
+    const int kpart = wave % KW;  // this wave's part of K (KW > 1)
+    const int slab = wave / KW;   // this wave's slab in the workgroup
 
-    // K range: the split's slice (and with KSPLIT_WAVES this wave's quarter).
+    // K range: the split's slice (with KW > 1 this wave's part of it).
     int k0 = s0, k1 = s1;
-    if (KSPLIT_WAVES) {
-        const int q = (s1 - s0 + 3) / 4;
-        k0 = min(s0 + wave * q, s1);
+    if (KW > 1) {
+        const int q = (s1 - s0 + KW - 1) / KW;
+        k0 = min(s0 + kpart * q, s1);
         k1 = min(k0 + q, s1);
     }
 
@@ -113,7 +117,7 @@ __device__ __forceinline__ void stream_tile(const bf16* __restrict__ A,
         const int arow = min(row0 + kFrag * f + j, row_end - 1);
         a_ptr[f] = A + (size_t)(a_rows ? a_rows[arow] : arow) * K + 8 * g;
     }
-    const int col = n_tile * TILE_N + (KSPLIT_WAVES ? 0 : wave * kSlab) + 8 * j;
+    const int col = n_tile * TILE_N + slab * kSlab + 8 * j;
     const bool b_ok = col < N;
     const size_t b_off = b_base + (size_t)(8 * g) * N + (b_ok ? col : 0);
     const bf16* b_ptr[NMAT];
@@ -217,28 +221,31 @@ __device__ __forceinline__ void stream_tile(const bf16* __restrict__ A,
         }
     }
 
-    if (KSPLIT_WAVES) {
-        // ---- add the four quarters
-        if (wave > 0) {
+    if (KW > 1) {
+        // ---- add the parts of K: the slab's first wave adds the others'
+        // partial sums in K order; LDS slot of wave w (part p > 0):
+        // (w / KW) (KW - 1) + p - 1
+        if (kpart > 0) {
+            const int slot = slab * (KW - 1) + kpart - 1;
 #pragma unroll
             for (int f = 0; f < MF; ++f)
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
-                        red[(wave - 1) * MF * NMAT * 8 + (f * NMAT + m) * 8 + c][lane] = acc[f][m][c];
+                        red[slot * MF * NMAT * 8 + (f * NMAT + m) * 8 + c][lane] = acc[f][m][c];
         }
         __syncthreads();
-        if (wave != 0) return;
+        if (kpart != 0) return;
 #pragma unroll
-        for (int w = 0; w < 3; ++w)
+        for (int w = 0; w < KW - 1; ++w)
 #pragma unroll
             for (int f = 0; f < MF; ++f)
 #pragma unroll
                 for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
-                        acc[f][m][c] += red[w * MF * NMAT * 8 + (f * NMAT + m) * 8 + c][lane];
+                        acc[f][m][c] += red[(slab * (KW - 1) + w) * MF * NMAT * 8 + (f * NMAT + m) * 8 + c][lane];
     }
 
     if (!b_ok) return;
@@ -268,20 +275,21 @@ __device__ __forceinline__ void stream_tile(const bf16* __restrict__ A,
         }
 }
 
-// Row tiles: KSPLIT_WAVES tiles hold 16 rows (MF = 1); otherwise up to 64,
+// Row tiles: with KW > 1 tiles hold 16 rows (MF = 1); otherwise up to 64,
 // with MF = 1, 2 or 4 by the tile's row count.
-template <bool KSPLIT_WAVES>
-constexpr int tile_rows() { return KSPLIT_WAVES ? kFrag : kFrag * kMaxFrags; }
+template <int KW>
+constexpr int tile_rows() { return KW > 1 ? kFrag : kFrag * kMaxFrags; }
 
-template <bool DUAL, bool KSPLIT_WAVES>
+template <bool DUAL, int KW>
 __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
     const bf16* __restrict__ A, const int32_t* __restrict__ a_rows, const bf16* __restrict__ B0,
     const bf16* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets, int R,
     int E, int K, int N, int splits) {
     constexpr int NMAT = DUAL ? 2 : 1;
-    constexpr int TILE_N = KSPLIT_WAVES ? kSlab : 4 * kSlab;
-    constexpr int TILE_M = tile_rows<KSPLIT_WAVES>();
-    __shared__ floatx4 red[KSPLIT_WAVES ? 3 * NMAT * 8 : 1][64];
+    constexpr int TILE_N = (4 / KW) * kSlab;
+    constexpr int TILE_M = tile_rows<KW>();
+    // partial sums of the waves past the first of each slab (MF = 1)
+    __shared__ floatx4 red[KW > 1 ? (4 - 4 / KW) * NMAT * 8 : 1][64];
 
     // ---- which (expert, split, n-tile, m-tile) this workgroup computes
     const int NT = (N + TILE_N - 1) / TILE_N;
@@ -318,34 +326,34 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(
     const int s0 = min(split * kt_split, KT);
     const int s1 = min(s0 + kt_split, KT);
     const size_t b_base = (size_t)e * K * N;
-    if (KSPLIT_WAVES) {
-        stream_tile<DUAL, true, 1>(A, a_rows, B0, B1, C, b_base, row0, row_end, n_tile, split, s0,
-                                   s1, R, K, N, red);
-        return;
+    if constexpr (KW > 1) {
+        stream_tile<DUAL, KW, 1>(A, a_rows, B0, B1, C, b_base, row0, row_end, n_tile, split, s0,
+                                 s1, R, K, N, red);
+    } else {
+        const int rows = min(row_end - row0, TILE_M);
+        if (rows <= kFrag)
+            stream_tile<DUAL, 1, 1>(A, a_rows, B0, B1, C, b_base, row0, row_end, n_tile, split,
+                                    s0, s1, R, K, N, red);
+        else if (rows <= 2 * kFrag)
+            stream_tile<DUAL, 1, 2>(A, a_rows, B0, B1, C, b_base, row0, row_end, n_tile, split,
+                                    s0, s1, R, K, N, red);
+        else
+            stream_tile<DUAL, 1, 4>(A, a_rows, B0, B1, C, b_base, row0, row_end, n_tile, split,
+                                    s0, s1, R, K, N, red);
     }
-    const int rows = min(row_end - row0, TILE_M);
-    if (rows <= kFrag)
-        stream_tile<DUAL, false, 1>(A, a_rows, B0, B1, C, b_base, row0, row_end, n_tile, split,
-                                    s0, s1, R, K, N, red);
-    else if (rows <= 2 * kFrag)
-        stream_tile<DUAL, false, 2>(A, a_rows, B0, B1, C, b_base, row0, row_end, n_tile, split,
-                                    s0, s1, R, K, N, red);
-    else
-        stream_tile<DUAL, false, 4>(A, a_rows, B0, B1, C, b_base, row0, row_end, n_tile, split,
-                                    s0, s1, R, K, N, red);
 }
 
-template <bool DUAL, bool KSPLIT_WAVES>
+template <bool DUAL, int KW>
 hipError_t launch_stream(const void* A, const int32_t* a_rows, const void* B0, const void* B1,
                          void* C, const int32_t* offsets, int R, int E, int K, int N, int splits,
                          hipStream_t stream) {
-    const long long tile_n = KSPLIT_WAVES ? kSlab : 4 * kSlab;
+    const long long tile_n = (4 / KW) * kSlab;
     const long long NT = (N + tile_n - 1) / tile_n;
-    const long long tile_m = tile_rows<KSPLIT_WAVES>();
+    const long long tile_m = tile_rows<KW>();
     const long long mtiles = (R + tile_m - 1) / tile_m + E;  // bound on sum_e ceil(n_e / tile_m)
     long long grid = mtiles * NT * splits;
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((stream_gemm_kernel<DUAL, KSPLIT_WAVES>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((stream_gemm_kernel<DUAL, KW>), dim3((unsigned)grid),
                        dim3(kThreads), 0, stream, reinterpret_cast<const bf16*>(A), a_rows,
                        reinterpret_cast<const bf16*>(B0), reinterpret_cast<const bf16*>(B1), C,
                        offsets, R, E, K, N, splits);
@@ -356,15 +364,17 @@ hipError_t launch_stream(const void* A, const int32_t* a_rows, const void* B0, c
 
 hipError_t launch_gemm1_swiglu_stream(const void* x, const int32_t* row_token, const void* w1,
                                       const void* w3, const int32_t* offsets, int R, int E, int d,
-                                      int f, bool ksplit_waves, void* h, hipStream_t stream) {
-    if (ksplit_waves)
-        return launch_stream<true, true>(x, row_token, w1, w3, h, offsets, R, E, d, f, 1, stream);
-    return launch_stream<true, false>(x, row_token, w1, w3, h, offsets, R, E, d, f, 1, stream);
+                                      int f, int k_waves, void* h, hipStream_t stream) {
+    if (k_waves == 4)
+        return launch_stream<true, 4>(x, row_token, w1, w3, h, offsets, R, E, d, f, 1, stream);
+    if (k_waves == 2)
+        return launch_stream<true, 2>(x, row_token, w1, w3, h, offsets, R, E, d, f, 1, stream);
+    return launch_stream<true, 1>(x, row_token, w1, w3, h, offsets, R, E, d, f, 1, stream);
 }
 
 hipError_t launch_gemm2_stream(const void* h, const void* w2, const int32_t* offsets, int R, int E,
                                int f, int d, int splits, float* y, hipStream_t stream) {
-    return launch_stream<false, false>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits,
+    return launch_stream<false, 1>(h, nullptr, w2, nullptr, y, offsets, R, E, f, d, splits,
                                        stream);
 }
 

@@ -57,6 +57,7 @@ SMALL = [
     (20, 256, 1024, 8, 2, torch.bfloat16),    # K split 8, one step per wave
     (5, 128, 128, 64, 8, torch.bfloat16),     # E = 64, most experts empty
     (2, 256, 1024, 8, 2, torch.bfloat16),     # GEMM 1 with K split over the waves
+    (2, 256, 4032, 64, 8, torch.bfloat16),    # GEMM 1 with K split over 2 waves per slab, partial last slab
     (110, 192, 320, 8, 2, torch.bfloat16),    # streamed, 2 row fragments per tile, ragged slabs
     (150, 256, 512, 8, 2, torch.bfloat16),    # streamed, 4 row fragments per tile
     (240, 256, 512, 8, 2, torch.bfloat16),    # 256-row tiles: tail tiles only (~60 rows per expert)
@@ -387,7 +388,7 @@ def mixtral_weights():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 64, 128, 207])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 8, 16, 64, 128, 207])
 def test_mixtral_shape_small_batches(T, mixtral_weights):
     """The batch sizes at the HBM-bound end of the batch sweep, at d=4096,
     f=14336, E=8, k=2, every token: the streamed kernels with GEMM 1's K
