@@ -1050,6 +1050,10 @@ def main():
         "note": ("each step streams the expert weights from HBM: one layer's 2.82 GB exceeds the "
                  "256 MiB MALL, so no cache flush is needed between steps"),
     }
+    overrides = {n: os.environ[n] for n in ("MOE_FFN_STREAM_SPLITS", "MOE_FFN_STREAM_K_WAVES")
+                 if os.environ.get(n)}
+    if overrides:
+        rec["plan_overrides"] = overrides
     side_counts = {}
 
     def side_workload(name):

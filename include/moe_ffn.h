@@ -39,6 +39,13 @@
  *   - The library keeps one cached workspace per device, grown on demand.
  *     Calls that use it from several host threads or streams at once race;
  *     such callers pass their own workspace through moe_ffn_forward_ex.
+ *   - Tuning overrides, read once per process from the environment (unset or
+ *     0: the library's own choice; results stay within the same tolerance,
+ *     only the summation split changes): MOE_FFN_STREAM_SPLITS = K slices of
+ *     the second expert GEMM on the few-rows-per-expert path (1..16, clamped
+ *     to f/128; the workspace grows by one T*k x d fp32 slice each), and
+ *     MOE_FFN_STREAM_K_WAVES = 1, 2 or 4 wavefronts splitting K per 128-column
+ *     slab in its first GEMM (at most 12 rows per expert).
  */
 #ifndef MOE_FFN_H
 #define MOE_FFN_H

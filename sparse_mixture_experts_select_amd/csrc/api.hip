@@ -19,6 +19,7 @@
 #include <cmath>
 #include <mutex>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -62,6 +63,23 @@ struct Plan {
 // faster; at two or more row tiles per expert 6-11% slower).
 constexpr int64_t kNtWeightRows = 192;
 
+// Overrides of the streamed path's kernel choices, for tuning runs:
+// MOE_FFN_STREAM_SPLITS sets GEMM 2's K slices (1..16, at most f/128) and
+// MOE_FFN_STREAM_K_WAVES the waves that split K per slab in GEMM 1 (1, 2 or
+// 4; 2 and 4 only where the tiles hold 16 rows, at most 12 rows per
+// expert).  Read once per process; unset or 0 keeps the plan's own choice.
+static int plan_override(int which) {
+    static const int splits = [] {
+        const char* v = getenv("MOE_FFN_STREAM_SPLITS");
+        return v ? atoi(v) : 0;
+    }();
+    static const int k_waves = [] {
+        const char* v = getenv("MOE_FFN_STREAM_K_WAVES");
+        return v ? atoi(v) : 0;
+    }();
+    return which == 0 ? splits : k_waves;
+}
+
 Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype) {
     Plan p;
     const int64_t R = T * k;
@@ -98,6 +116,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
                         break;
                     }
                 }
+                const int kw_o = plan_override(1);
+                if (kw_o == 1 || kw_o == 2 || kw_o == 4) p.g1_k_waves = kw_o;
             }
             // GEMM 2 gives each wave a 128-column slab, the 4 waves of a
             // workgroup 4 adjacent slabs (512 contiguous columns of every w2
@@ -118,6 +138,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k, int dtype)
             int64_t smax = f / 128;
             if (smax > 16) smax = 16;
             if (smax < 1) smax = 1;
+            if (plan_override(0) > 0) s = plan_override(0);
             if (s > smax) s = smax;
             if (s < 1) s = 1;
             p.splits = (int)s;

@@ -188,3 +188,39 @@ def test_unknown_dtype_codes_are_refused(binding):
     assert lib.moe_ffn_workspace_bytes(8, 128, 128, 8, 2, binding.MOE_DTYPE_BF16) > 0
     p = ctypes.c_void_p(ALIGNED)
     assert lib.moe_rmsnorm(p, p, 4, 128, ctypes.c_float(1e-5), 7, None) == binding.MOE_ERR_INVALID_ARG
+
+
+def _workspace_in_fresh_process(env_extra, args):
+    """moe_ffn_workspace_bytes(*args) for bf16 in a new interpreter with
+    extra environment variables (the plan overrides are read once per
+    process)."""
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("MOE_FFN_STREAM_SPLITS", None)
+    env.pop("MOE_FFN_STREAM_K_WAVES", None)
+    env.update(env_extra)
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from sparse_mixture_experts_select_amd import binding as b\n"
+            "print(b.moe_ffn_workspace_bytes(%s, b.MOE_DTYPE_BF16))\n" % (ROOT, ", ".join(map(str, args))))
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         timeout=120, check=True)
+    return int(out.stdout.strip().splitlines()[-1])
+
+
+def test_stream_splits_override():
+    """MOE_FFN_STREAM_SPLITS sets the number of fp32 K-slice partials of y
+    the streamed path keeps (one R x d slice each); values past the limit
+    (16, and f/128) are clamped, and the tile path ignores it."""
+    T, d, f, E, k = 32, 4096, 14336, 8, 2
+    R = T * k
+    base = _workspace_in_fresh_process({}, (T, d, f, E, k))
+    one = _workspace_in_fresh_process({"MOE_FFN_STREAM_SPLITS": "1"}, (T, d, f, E, k))
+    six = _workspace_in_fresh_process({"MOE_FFN_STREAM_SPLITS": "6"}, (T, d, f, E, k))
+    big = _workspace_in_fresh_process({"MOE_FFN_STREAM_SPLITS": "99"}, (T, d, f, E, k))
+    assert six - one == 5 * R * d * 4
+    assert base - one == 2 * R * d * 4  # the plan's own choice at decode: 3 slices
+    assert big - one == 15 * R * d * 4  # clamped to 16
+    pre = (4096, d, f, E, k)
+    assert (_workspace_in_fresh_process({"MOE_FFN_STREAM_SPLITS": "6"}, pre)
+            == _workspace_in_fresh_process({}, pre))
