@@ -524,12 +524,15 @@ moe_status_t moe_ffn_profile_begin(int32_t max_calls, uint32_t stage_mask) {
     if (g_prof.active) return fail(MOE_ERR_INVALID_ARG, "profiling already active");
     const size_t n = (size_t)max_calls * (MOE_NUM_STAGES + 1);
     hipEvent_t* ev = new hipEvent_t[n];
+    // Timing-only events: a device-scope release when recorded, so a record
+    // between two kernels does not write the L2 back to memory first (the
+    // default system-scope release would, adding that time to the stream).
     for (size_t i = 0; i < n; ++i) {
-        const hipError_t e = hipEventCreate(&ev[i]);
+        const hipError_t e = hipEventCreateWithFlags(&ev[i], hipEventReleaseToDevice);
         if (e != hipSuccess) {
             for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
             delete[] ev;
-            return hip_fail(e, "hipEventCreate");
+            return hip_fail(e, "hipEventCreateWithFlags");
         }
     }
     g_prof.ev = ev;
