@@ -159,6 +159,38 @@ def test_tiles_by_row_fragments(T, d, f, E, k, pieces):
     np.testing.assert_array_equal(PT.to_np(r["gpu"]["counts"]), [rows] * E)
     print("near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
 
+
+MODEL_SHAPES = [
+    # label, T, d, f, E, k, tokens checked: all, or those reaching every
+    # 128-row block of every expert's rows
+    ("d6144 f16384 E8 k2 streamed", 16, 6144, 16384, 8, 2, "all"),     # router with d > 4096
+    ("d6144 f16384 E8 k2 tiles", 1024, 6144, 16384, 8, 2, "blocks"),
+    ("d2048 f1408 E64 k6 streamed", 256, 2048, 1408, 64, 6, "all"),    # fine-grained experts
+    ("d2048 f1408 E64 k6 tiles", 2048, 2048, 1408, 64, 6, "blocks"),
+    ("d3584 f2560 E64 k8 streamed", 128, 3584, 2560, 64, 8, "all"),    # d, f not powers of 2
+    ("d3584 f2560 E64 k8 tiles", 1024, 3584, 2560, 64, 8, "blocks"),
+]
+
+
+@pytest.mark.parametrize("label,T,d,f,E,k,which", MODEL_SHAPES, ids=[m[0] for m in MODEL_SHAPES])
+def test_other_model_shapes(label, T, d, f, E, k, which):
+    """Published MoE configurations other than the Mixtral 8x7B one: a
+    larger hidden size (the router's general kernel, d > 4096), 64
+    fine-grained experts with k = 6 and 8, and hidden / expert sizes that
+    are not powers of two, each on the few-rows-per-expert path and on the
+    256-row tile path (by T)."""
+    banner("%s: T=%d d=%d f=%d E=%d k=%d" % (label, T, d, f, E, k))
+    inp = case(T, d, f, E, torch.bfloat16, seed=d + f + E + k, label="model")
+    tokens = None if which == "all" else (lambda g: PT.segment_sample_tokens(g, 5))
+    r = PT.full_check(inp, k, tokens=tokens, label=label)
+    R = T * k
+    streamed = R < 52 * E
+    assert streamed == ("streamed" in label)
+    print("near ties", r["near_ties"], "tokens checked", len(r["tokens"]), "err", r["err_out"],
+          r["err_h"], r["err_y"])
+    del inp, r
+    torch.cuda.empty_cache()
+
 def test_batch_with_h_past_2gib():
     """h = 65600 x 16384 bf16 is past 2 GiB: the GEMMs fall back from the
     256-row tile kernels (32-bit buffer offsets) to the 128-row grouped ones."""
