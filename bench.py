@@ -19,7 +19,11 @@ events around each step for the per-step median, minimum and 90th percentile
 ("step_ms").
 
 The CPU baseline times the fp64 oracle on the host on a bounded sample of the
-same workload.
+same workload.  Beside the layer the line carries the measured ceilings of this
+part (the read probe over the decode layer's own weights, the MFMA probe), the
+prefill experts' GEMM products timed with torch.matmul for comparison
+("vendor_gemm"; nothing in the layer calls it) and any plan overrides set in
+the environment ("plan_overrides").
 """
 from __future__ import annotations
 
