@@ -36,7 +36,9 @@ def run_stack(st, h, x, k, fused=False):
 
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("T,d,f", [(300, 256, 512),    # 256-row tile path
-                                   (24, 256, 1024)])   # streamed-weight path
+                                   (768, 1024, 2048),  # tiles, GEMM 2's last round cut into K pieces
+                                   (24, 256, 1024),    # streamed-weight path
+                                   (2, 256, 8448)])    # streamed, GEMM 1 with 2 waves per slab
 def test_graph_replay_matches_eager(T, d, f, fused):
     print("\n[case] graph of 4 blocks T=%d d=%d f=%d fused=%s" % (T, d, f, fused), flush=True)
     E, k = 8, 2
