@@ -666,6 +666,115 @@ def vendor_gemm(torch, wl, counts, ours, reps=10):
     return out
 
 
+POWER_COMMAND = "python3 bench.py --power-sample {secs}"
+
+
+def power_sample(torch, binding, inputs, secs=10.0):
+    """Board power while the layer runs: `amd-smi metric -p` polled in a
+    thread (socket power, about four readings a second) during loops of the
+    decode layer, the prefill layer and the MFMA probe, each about `secs`
+    seconds after a short warm-up, with the power cap from `rocm-smi
+    --showmaxpower`; written to profiles/board_power_decode_prefill_mfma.txt.
+    A measurement aid only; the library does not read power."""
+    import re
+    import shutil
+    import statistics
+    import subprocess
+    import threading
+
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    rsmi = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    cap = None
+    try:
+        txt = subprocess.run([rsmi, "--showmaxpower"], capture_output=True, text=True, timeout=30).stdout
+        m = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", txt)
+        cap = float(m.group(1)) if m else None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    samples = []
+    on = threading.Event()
+    on.set()
+
+    def poll():
+        while on.is_set():
+            try:
+                txt = subprocess.run([smi, "metric", "-p"], capture_output=True, text=True, timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+            if m:
+                samples.append((time.time(), float(m.group(1))))
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    phases = []
+
+    def phase(name, body):
+        body(1.0)  # warm-up, not counted
+        t0 = time.time()
+        info = body(secs)
+        phases.append((name, t0, time.time(), info))
+
+    def idle(t):
+        time.sleep(t)
+        return ""
+
+    def layer(which):
+        wl = inputs.WORKLOADS[which]
+        inp = inputs.workload_inputs(which, "cuda")
+        out = torch.empty_like(inp["x"])
+
+        def body(t):
+            t0, n = time.time(), 0
+            while time.time() - t0 < t:
+                for _ in range(20):
+                    binding.moe_ffn_forward(inp["x"], inp["w_router"], inp["w1"], inp["w3"], inp["w2"],
+                                            wl.k, out=out)
+                torch.cuda.synchronize()
+                n += 20
+            return "%.4f ms/step" % (1e3 * (time.time() - t0) / n)
+        return body, inp
+
+    phase("idle", idle)
+    for which in ("decode", "prefill"):
+        body, inp = layer(which)
+        phase(which, body)
+        del inp, body
+        torch.cuda.empty_cache()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ops = torch.randn(4 << 20, dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
+
+    def mfma(t):
+        t0 = time.time()
+        while time.time() - t0 < t:
+            binding.moe_mfma_probe(ops, 20000, cus, sink, clocks)
+            torch.cuda.synchronize()
+        ck = clocks.cpu().numpy().reshape(cus, 2).astype(float)
+        return "clock %.3f GHz" % (ck[:, 0].sum() / ck[:, 1].sum() * 0.1)
+
+    phase("mfma_probe", mfma)
+    on.clear()
+    th.join(timeout=15)
+    out = os.path.join(ROOT, "profiles", "board_power_decode_prefill_mfma.txt")
+    with open(out, "w") as fh:
+        fh.write("# Board (socket) power while the layer runs: amd-smi metric -p polled during %.0f s loops "
+                 "of the decode layer (T=32), the prefill layer (T=4096) and the MFMA probe\n" % secs)
+        fh.write("# command: %s\n" % POWER_COMMAND.format(secs=int(secs)))
+        fh.write("power_cap_w = %s  (rocm-smi --showmaxpower: Max Graphics Package Power)\n" % cap)
+        for name, t0, t1, info in phases:
+            w = [v for (t, v) in samples if t0 + 0.5 <= t <= t1]
+            if not w:
+                fh.write("%s: no readings\n" % name)
+                continue
+            fh.write("%s: median %.0f W, min %.0f, max %.0f, %d readings%s%s\n" % (
+                name, statistics.median(w), min(w), max(w), len(w),
+                (", %.3f of the cap" % (statistics.median(w) / cap)) if cap else "",
+                ("; " + info) if info else ""))
+    log("[bench] wrote", out)
+
+
 def calibrate_copy(torch, nbytes=CALIBRATION_BYTES, reps=3):
     """Plain device-to-device copies of a known size (reference for the
     FETCH_SIZE / WRITE_SIZE counters)."""
@@ -991,6 +1100,9 @@ def main():
                          "SKEWED_PMC_COMMAND or STACK_PMC_COMMAND")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--power-sample", type=float, metavar="SECONDS",
+                    help="only sample board power during decode, prefill and MFMA-probe loops of "
+                         "this length and write the profile")
     ap.add_argument("--summarize-stalls", nargs=4, metavar="PMC_DIR",
                     help="the four counter passes of STALL_COMMAND, in STALL_PASSES order")
     args = ap.parse_args()
@@ -1020,6 +1132,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.power_sample:
+        power_sample(torch, binding, inputs, args.power_sample)
+        return
 
     prim = run_workload(args.workload, args.steps, args.warmup, binding, inputs, torch)
     bound = "hbm" if args.workload == "decode" else "mfma"
