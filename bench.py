@@ -170,13 +170,18 @@ def stage_rooflines(wl, counts, stage_ms, decode):
 def source_digest(workload):
     """Digest of the source of the w1/w3 kernel the workload runs (plus the
     headers it includes from the library), to tell whether committed counter
-    figures still apply."""
+    figures still apply.  Comments and whitespace are left out, so an edit
+    of the comments alone keeps the figures."""
+    import re
     h = hashlib.sha256()
     src = GEMM1_KERNEL[workload][0]
     headers = ("common.h", "tile_order.h", "gemm_tile.hip") if src == "tile_gemm.h" else ("common.h",)
     for name in (src,) + headers:
-        with open(os.path.join(CSRC, name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, name)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

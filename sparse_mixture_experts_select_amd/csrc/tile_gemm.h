@@ -512,6 +512,9 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         // multiplied (the rest stay zero and are never stored): a tail tile
         // (the expert's last 1..128 rows, the same rows in every wave) takes
         // 2, 4, 6 or 8 of them, a full tile with at most 192 rows 6 per wave.
+        // MOE_K_LOOP(A loads and B loads per lane and step, B's offset in a
+        // stage, fragments per wave, bytes between a wave's fragments in a
+        // stage, DMA loads placed among MFMA groups 4..7).
         const int tile_rows = min(row_end - row0, 256);
         if (!is_tail) {
             if (tile_rows <= 192) MOE_K_LOOP(4, 4, kBOffFull, 6, 32 * 64, 2, 2, 2, 2)
