@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 
 #define MOE_MFMAS(N_, BF_, MF_)                                                             \
     _Pragma("unroll") for (int m_ = 0; m_ < (MF_); ++m_)                                    \
-        acc[m_][N_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[m_], BF_, acc[m_][N_], 0, 0, 0)
+        acc[m_][N_] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afc_[m_], BF_, acc[m_][N_], 0, 0, 0)
 
 // Scheduling hints: within a group of 8 (or 6) MFMAs, put one of the group's
 // LDS reads (for fragments two groups ahead) after each of the first NR_
@@ -401,23 +401,26 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                              \
     }
 
-    // One K step on stage CUR_.  On entry af[] holds its A fragments and
+    // One K step on stage CUR_.  On entry AF_ holds its A fragments and
     // bq0, bq1 its first two B fragments; B fragment n + 2 is read while the
     // MFMAs of fragment n run.  Half way (before fragment 4): wait until this
     // wave's loads of the next stage NXT_ are complete (vmcnt(NV_): only the
     // stage after it may still be in flight), barrier (now every wave's loads
     // of NXT_ have landed, and every wave has consumed its reads of REF_, the
     // stage of the previous step), refill REF_ with step kt + 3, and read the
-    // next step's A fragments and first two B fragments from NXT_ under the
-    // remaining MFMAs.
+    // next step's A fragments (into AN_) and first two B fragments from NXT_
+    // under the remaining MFMAs.  The two A arrays trade roles from step to
+    // step (the unroll by four names them), so no register copy moves the
+    // fragments between steps.
     // A step past the end of the slice (the last loop iteration may hold up
     // to three) skips its reads and MFMAs but still waits, takes the barrier
     // and issues its (repeated, never read) refill, so every path through the
     // loop issues the same sequence of DMA loads: the compiler's DMA wait
     // tracking then stays per stage across the guards' control-flow merges.
-#define MOE_STEP(CUR_, NXT_, REF_, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)                \
+#define MOE_STEP(CUR_, NXT_, REF_, AF_, AN_, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)    \
     {                                                                                       \
         const lds_char* st_ = (const lds_char*)(lds_void*)(CUR_);                           \
+        bf16x8(&afc_)[8] = (AF_);                                                           \
         const bool live_ = kt < kt1;                                                        \
         bf16x8 b4_, b5_;                                                                    \
         if (live_) {                                                                        \
@@ -446,19 +449,18 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         MOE_ISSUE_STAGE(min(kt + 3, kt1 - 1), REF_, NA_, NB_, BOFF_);                       \
         if (live_) {                                                                        \
             const lds_char* sn_ = (const lds_char*)(lds_void*)(NXT_);                       \
-            bf16x8 an[8];                                                                   \
             const bf16x8 b6_ = MOE_READ_B(st_, 6);                                          \
-            if constexpr (0 < (MF_)) an[0] = MOE_READ_A(NXT_, 0);                           \
-            if constexpr (1 < (MF_)) an[1] = MOE_READ_A(NXT_, 1);                           \
+            if constexpr (0 < (MF_)) AN_[0] = MOE_READ_A(NXT_, 0);                           \
+            if constexpr (1 < (MF_)) AN_[1] = MOE_READ_A(NXT_, 1);                           \
             MOE_MFMAS(4, b4_, MF_);                                                         \
             const bf16x8 b7_ = MOE_READ_B(st_, 7);                                          \
-            if constexpr (2 < (MF_)) an[2] = MOE_READ_A(NXT_, 2);                           \
-            if constexpr (3 < (MF_)) an[3] = MOE_READ_A(NXT_, 3);                           \
+            if constexpr (2 < (MF_)) AN_[2] = MOE_READ_A(NXT_, 2);                           \
+            if constexpr (3 < (MF_)) AN_[3] = MOE_READ_A(NXT_, 3);                           \
             MOE_MFMAS(5, b5_, MF_);                                                         \
-            if constexpr (4 < (MF_)) an[4] = MOE_READ_A(NXT_, 4);                           \
-            if constexpr (5 < (MF_)) an[5] = MOE_READ_A(NXT_, 5);                           \
-            if constexpr (6 < (MF_)) an[6] = MOE_READ_A(NXT_, 6);                           \
-            if constexpr (7 < (MF_)) an[7] = MOE_READ_A(NXT_, 7);                           \
+            if constexpr (4 < (MF_)) AN_[4] = MOE_READ_A(NXT_, 4);                           \
+            if constexpr (5 < (MF_)) AN_[5] = MOE_READ_A(NXT_, 5);                           \
+            if constexpr (6 < (MF_)) AN_[6] = MOE_READ_A(NXT_, 6);                           \
+            if constexpr (7 < (MF_)) AN_[7] = MOE_READ_A(NXT_, 7);                           \
             bq0 = MOE_READ_B(sn_, 0);                                                       \
             MOE_MFMAS(6, b6_, MF_);                                                         \
             bq1 = MOE_READ_B(sn_, 1);                                                       \
@@ -474,7 +476,6 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
                 MOE_SCHED_GROUP6(4, G6_);                                                   \
                 MOE_SCHED_GROUP6(2, G7_);                                                   \
             }                                                                               \
-            _Pragma("unroll") for (int m_ = 0; m_ < (MF_); ++m_) af[m_] = an[m_];           \
         }                                                                                   \
         ++kt;                                                                               \
     }
@@ -493,16 +494,16 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
         MOE_ISSUE_STAGE(min(kt0 + 2, kt1 - 1), st2, NA_, NB_, BOFF_);                       \
         MOE_WAIT_VM(2 * ((NA_) + (NB_)));                                                   \
         stage_barrier();                                                                    \
-        bf16x8 af[8];                                                                       \
-        _Pragma("unroll") for (int m = 0; m < (MF_); ++m) af[m] = MOE_READ_A(st0, m);       \
+        bf16x8 af0[8], af1[8];                                                              \
+        _Pragma("unroll") for (int m = 0; m < (MF_); ++m) af0[m] = MOE_READ_A(st0, m);      \
         const lds_char* s0_ = (const lds_char*)(lds_void*)st0;                              \
         bf16x8 bq0 = MOE_READ_B(s0_, 0);                                                    \
         bf16x8 bq1 = MOE_READ_B(s0_, 1);                                                    \
         while (kt < kt1) {                                                                  \
-            MOE_STEP(st0, st1, st3, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)               \
-            MOE_STEP(st1, st2, st0, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)               \
-            MOE_STEP(st2, st3, st1, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)               \
-            MOE_STEP(st3, st0, st2, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)               \
+            MOE_STEP(st0, st1, st3, af0, af1, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)     \
+            MOE_STEP(st1, st2, st0, af1, af0, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)     \
+            MOE_STEP(st2, st3, st1, af0, af1, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)     \
+            MOE_STEP(st3, st0, st2, af1, af0, NA_, NB_, BOFF_, MF_, G4_, G5_, G6_, G7_)     \
         }                                                                                   \
     }
 
