@@ -263,7 +263,9 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform, so the DMA loads' LDS destinations (M0) are formed in
+    // scalar registers instead of being read back from a vector register
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1;
     const int wn = wave & 1;
     const int lrow = lane & 15;
