@@ -65,6 +65,9 @@ SMALL = [
     (1500, 1024, 2048, 8, 2, torch.bfloat16), # GEMM 2 tiles cut into 3 K pieces, several per XCD
     (2600, 768, 704, 2, 2, torch.bfloat16),   # 10 row tiles + a tail per expert: a partial block of
                                               # row tiles, partial column-tile groups in both GEMMs
+    (1100, 320, 384, 8, 2, torch.bfloat16),   # GEMM 2: a whole column tile + one of 64 columns
+    (2000, 704, 256, 8, 2, torch.bfloat16),   # GEMM 2: two whole column tiles + one of 192 columns
+    (1300, 1152, 512, 4, 2, torch.bfloat16),  # partial last row tiles of ~138 rows (6 fragments per wave row)
     (50, 100, 60, 5, 2, torch.float32),
     (200, 64, 96, 16, 4, torch.float32),
     # multi-workgroup route scan (over 4096 assignments) with wide routing
