@@ -25,8 +25,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// SiLU(z) = z * sigmoid(z), fp32.
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z * sigmoid(z), fp32, with the sigmoid's reciprocal taken by
+// v_rcp_f32 (1 ulp) rather than an IEEE division (about ten VALU instructions
+// per value in the GEMM 1 epilogues); h is rounded to bf16 right after, or
+// kept in fp32 within 1 ulp.  Large |z| keep their limits: exp(-z) = inf
+// gives z * 0 = -0, exp(-z) = 0 gives z.
+__device__ __forceinline__ float silu_f32(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Kernel launchers.  Each returns the hipGetLastError() of its launch(es).
 // dtype: 0 = bf16, 1 = fp32 (same codes as moe_dtype_t).
