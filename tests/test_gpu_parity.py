@@ -244,6 +244,26 @@ def test_streamed_path_with_one_heavy_expert(T):
     assert PT.to_np(r["gpu"]["counts"])[2] == T
 
 
+@pytest.mark.parametrize("T,d,f,E,k,dtype", [
+    (40, 256, 384, 8, 2, torch.bfloat16),    # streamed GEMMs
+    (600, 192, 320, 8, 2, torch.bfloat16),   # 256-row tiles
+    (50, 128, 96, 8, 2, torch.float32),      # fp32 GEMMs
+])
+def test_saturated_silu(T, d, f, E, k, dtype):
+    """w1 scaled by 200, so its pre-activations reach the hundreds while the
+    router's logits keep their scale: SiLU's exp(-z) overflows fp32 for z
+    below about -88 (its sigmoid factor then has to come out as 0, h as -0)
+    and underflows for large z (factor 1, h = z * b).  Every element of out,
+    h and y against the oracle."""
+    banner("saturated SiLU T=%d d=%d f=%d E=%d k=%d %s" % (T, d, f, E, k, dtype))
+    inp = case(T, d, f, E, dtype, seed=T + d + f + 7, label="saturated")
+    inp["w1"] = (inp["w1"].float() * 200.0).to(dtype)
+    r = PT.full_check(inp, k)
+    h = PT.out_f64(r["gpu"]["h"])
+    assert np.all(np.isfinite(h)) and np.abs(h).max() > 100
+    print("near ties", r["near_ties"], "err", r["err_out"], r["err_h"], r["err_y"])
+
+
 def test_zero_tokens_leaves_out_untouched():
     from sparse_mixture_experts_select_amd import binding
     inp = case(0, 128, 128, 8, torch.bfloat16, seed=1, label="empty")
