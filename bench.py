@@ -934,7 +934,7 @@ def summarize_stalls(run_dirs):
     import statistics
 
     kernels = (("w1/w3 grouped GEMM + SwiGLU", GEMM1_KERNEL["prefill"][1]),
-               ("w2 grouped GEMM", r"tile_gemm_kernel(<false, true>|ILb0ELb1E)"))
+               ("w2 grouped GEMM", r"tile_gemm_kernel(<false, (true|false)>|ILb0ELb[01]E)"))
     per = {name: {} for name, _ in kernels}
     span = {name: {} for name, _ in kernels}
     for d in run_dirs:
